@@ -1,0 +1,141 @@
+"""Attention: the staged-precision online-softmax recipe and an fp64 brute
+force (test infrastructure).
+
+Definition [FV §2.1]: Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V.
+FlashAttention [FA4, FlashAttention section]: the keys are visited tile by tile
+and the softmax is normalised while it is computed (online softmax), so no
+N x N matrix is kept.  [FA4, co-design list: conditional softmax rescaling]
+the running output is rescaled only when the running maximum moves; with a
+threshold of zero this changes nothing numerically (a factor of exactly 1),
+so the recipe below rescales unconditionally.
+[FPS §3.1] P is quantised per tensor to FP8 with the fixed scale 1/448:
+P~ = E4M3(448 * P) and P ~= P~ / 448.
+
+Recipe, one query row i of one (batch, head), key tiles of BN keys visited in
+ascending order (for sliding-tile attention: the tiles of the query's window
+list in ascending order; causal: keys j <= i; padded keys masked):
+  m = -inf, l = 0, acc = 0
+  per tile:
+    S_j   = fl32( (sum_k dec(qQ_ik) dec(qK_jk)) / (s_Q(i) s_K(j)) * sm_scale * log2(e) )
+            (MXFP4: the per-32 scales 2^(eQ+eK) sit inside the sum);
+            masked keys get S_j = -inf; a tile without a valid key is skipped
+    m'    = max(m, max_j S_j);   alpha = 2^(m - m')  (1 when m' == m)
+    P_j   = fl32(2^(S_j - m'))                      (so 0 <= P_j <= 1)
+    l     = alpha l + sum_j P_j                      (P before quantisation)
+    P~_j  = E4M3(fl32(448 P_j))
+    acc_c = alpha acc_c + sum_j dec(P~_j) dec(qV_jc) (float64)
+    m     = m'
+  O_ic = fl32(acc_c / l / 448 / s_V(c)); a row with no valid key gives 0.
+The products of decoded FP8 codes are exact in float64 and so are their sums
+at these lengths, so a float64 matrix product serves as the exact sum.
+"""
+import numpy as np
+
+from .formats import e4m3_decode, e4m3_encode, e2m1_decode
+
+LOG2E = 1.4426950408889634
+
+
+class Operand:
+    """One quantised (batch, head) operand in the kernel's token order.
+
+    kind 'fp8_block':   codes [N, d] uint8 E4M3, scales [ceil(N/blk)] float32
+    kind 'mxfp4':       codes [N, d] uint8 4-bit E2M1, scales [N, d/32] uint8 E8M0
+    kind 'fp8_channel': codes [N, d] uint8 E4M3, scales [d] float32
+    """
+
+    def __init__(self, kind, codes, scales, blk=None):
+        self.kind, self.codes, self.scales, self.blk = kind, codes, scales, blk
+
+
+def _decoded(op, rows):
+    """Decoded values (float64) of the given token rows, and the per-row
+    divisor (float64, 1 for MXFP4 whose scales are applied inside)."""
+    if op.kind == "fp8_block":
+        vals = e4m3_decode(op.codes[rows])
+        div = op.scales[rows // op.blk].astype(np.float64)
+        return vals, div
+    if op.kind == "mxfp4":
+        vals = e2m1_decode(op.codes[rows])
+        d = vals.shape[-1]
+        sc = np.ldexp(1.0, op.scales[rows].astype(np.int64) - 127)
+        vals = (vals.reshape(len(rows), d // 32, 32) * sc[..., None]).reshape(len(rows), d)
+        return vals, np.ones(len(rows))
+    raise ValueError(op.kind)
+
+
+def scores(q, k, qrows, kcols, sm_scale, fp64_core=False):
+    """S' for the given query rows x key columns (log2 domain), float32
+    (float64 when fp64_core)."""
+    qv, qdiv = _decoded(q, qrows)
+    kv, kdiv = _decoded(k, kcols)
+    s = (qv @ kv.T) / (qdiv[:, None] * kdiv[None, :]) * (sm_scale * LOG2E)
+    return s if fp64_core else s.astype(np.float32)
+
+
+def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None,
+                     key_blocks=None, quantize_p=True, fp64_core=False):
+    """Output rows O[rows, :] (float32) of one (batch, head).
+
+    key_blocks: None (all BN-key tiles 0..ceil(N/BN)-1) or an ascending list of
+    key-tile start indices shared by every row in `rows`.
+    quantize_p=False / fp64_core=True switch parts of the recipe off so that
+    tests can pin the online-softmax core against the brute force.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    n, d = k.codes.shape
+    r = len(rows)
+    ftype = np.float64 if fp64_core else np.float32
+    m = np.full(r, -np.inf, dtype=ftype)
+    l = np.zeros(r)
+    acc = np.zeros((r, d))
+    vdec = e4m3_decode(v.codes)
+    if key_blocks is None:
+        key_blocks = range(0, n, bn)
+    for t0 in key_blocks:
+        cols = np.arange(t0, min(n, t0 + bn))
+        s = scores(q, k, rows, cols, sm_scale, fp64_core)
+        valid = np.ones((r, len(cols)), dtype=bool)
+        if kv_valid is not None:
+            valid &= kv_valid[cols][None, :].astype(bool)
+        if causal:
+            valid &= cols[None, :] <= rows[:, None]
+        s = np.where(valid, s, -np.inf).astype(ftype)
+        tmax = s.max(axis=1)
+        has = valid.any(axis=1)
+        m_new = np.where(has, np.maximum(m, tmax), m).astype(ftype)
+        with np.errstate(invalid="ignore"):
+            alpha = np.where(m_new == m, 1.0,
+                             np.exp2(m.astype(np.float64) - m_new.astype(np.float64)))
+            p = np.exp2(s.astype(np.float64) - m_new.astype(np.float64)[:, None])
+        p = np.where(valid, p, 0.0)
+        if not fp64_core:
+            p = p.astype(np.float32)
+        l = alpha * l + p.astype(np.float64).sum(axis=1)
+        if quantize_p:
+            pq = e4m3_decode(e4m3_encode(np.float32(448.0) * p.astype(np.float32)))
+        else:
+            pq = 448.0 * p.astype(np.float64)
+        acc = alpha[:, None] * acc + pq @ vdec[cols]
+        m = m_new
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o = acc / l[:, None] / 448.0 / v.scales.astype(np.float64)[None, :]
+    o = np.where((l > 0)[:, None], o, 0.0)
+    return o.astype(np.float32)
+
+
+def brute_force(q, k, v, sm_scale, mask=None):
+    """softmax(q k^T * sm_scale) v in float64 with the natural exponential;
+    mask[i, j] False removes key j for query i; a fully masked row gives 0."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    s = (q @ k.T) * sm_scale
+    if mask is not None:
+        s = np.where(mask, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    ok = np.isfinite(mx[:, 0])
+    mx = np.where(np.isfinite(mx), mx, 0.0)
+    e = np.exp(s - mx)
+    den = e.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o = (e @ v) / den
+    return np.where(ok[:, None], o, 0.0)
