@@ -1,0 +1,222 @@
+/*
+ * pab.h - C ABI of libpab: block-scaled FP8 / MXFP4 FlashAttention forward
+ * with optional 3D sliding-tile sparsity, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *  [FPS]  "FP8量化与稀疏性协同加速视频扩散模型" (FPSAttention): §2.1 block FP8
+ *         quantisation, §2.2 sliding-tile attention, §3.1 staged quantisation
+ *         strategy, §3.3 kernel design (block transpose, fusion).
+ *  [FP4G] "Blackwell架构实战：如何用FP4量化让你的AI模型推理速度翻倍（附代码）",
+ *         §1: E2M1 and micro-scaled (MX) 4-bit quantisation.
+ *  [FA4]  "FA4极速LLM：10分钟搞定20倍内存直降！": tiling, online softmax,
+ *         conditional rescaling, LPT scheduling for causal masks.
+ *  [FV]   FastVideo FP4 attention kernel article (wmrh.cn): §2.1 attention
+ *         definition, §5.2 the fp4_attention(qkv, mask, head_dim,
+ *         scaling_factor) call, §8.2 fall back when the output is not finite.
+ *
+ * Conventions for every call
+ *  - Tensors are in device memory the caller allocated; the library never
+ *    allocates device memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every device call is asynchronous on that stream and does not
+ *    synchronise, except when the environment variable PAB_SYNC_DEBUG=1 is
+ *    set (then each call synchronises the stream and reports kernel errors).
+ *  - All arguments are validated before any launch; a call that returns an
+ *    error other than PAB_HIP_ERROR has written nothing.
+ *  - Element counts and strides are in elements, not bytes.
+ *  - Quantised token buffers are padded: a tensor with n tokens is stored with
+ *    n_alloc = pab_token_alloc(n) token slots (a multiple of PAB_TOKEN_ALIGN);
+ *    the quantizers write zero codes into slots n..n_alloc-1.
+ *  - No C++ exception crosses this interface.  Thread-safe (no globals other
+ *    than the thread-local last HIP error).
+ */
+#ifndef PAB_H
+#define PAB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PAB_ABI_VERSION 1
+#define PAB_TOKEN_ALIGN 128  /* query tile of the attention kernel */
+
+typedef enum {
+  PAB_OK = 0,
+  PAB_INVALID_ARG = 1,   /* null pointer, bad shape, stride or size */
+  PAB_UNSUPPORTED = 2,   /* valid but not implemented (e.g. d not in {64,128}) */
+  PAB_HIP_ERROR = 3      /* a HIP runtime call failed; see pab_last_hip_error */
+} pab_status;
+
+typedef enum { PAB_F32 = 0, PAB_BF16 = 1 } pab_dtype;
+
+/* Quantisation recipes of the staged precision strategy [FPS §3.1] and the
+ * MX variant [FP4G §1]. */
+typedef enum {
+  /* Q/K: FP8 E4M3 (OCP "fn", largest 448), one fp32 scale per block of
+   * `block_tokens` consecutive tokens x all d channels of one (batch, head):
+   * s = fl32(448 / amax) (s = 1 if amax is 0 or the quotient is not finite),
+   * code = E4M3(fl32(x * s)), round-to-nearest-even, saturating at +-448;
+   * dequantised x ~= decode(code) / s  [FPS §2.1]. */
+  PAB_FP8_TOKEN_BLOCK = 0,
+  /* V: FP8 E4M3 with one fp32 scale per (batch, head, channel) over all tokens,
+   * same scale rule [FPS §3.1]. */
+  PAB_FP8_CHANNEL = 1,
+  /* Q/K MXFP4: E2M1 codes with one E8M0 scale per 32 consecutive channels:
+   * e = clamp(floor(log2 amax) - 2, -127, 127) (-127 for an all-zero group),
+   * scale byte e + 127, code = E2M1(x * 2^-e), round-to-nearest-even on the
+   * code, saturating at +-6; dequantised x = decode(code) * 2^e [FP4G §1]. */
+  PAB_MXFP4_D32 = 2
+} pab_recipe;
+
+/* ABI version (PAB_ABI_VERSION of the built library). */
+int pab_abi_version(void);
+/* Static description of a status code. */
+const char* pab_status_str(pab_status s);
+/* hipError_t of the last failing HIP call on this thread (0 if none). */
+int pab_last_hip_error(void);
+/* Token slots a quantised buffer for n tokens must hold (n rounded up to
+ * PAB_TOKEN_ALIGN). */
+int64_t pab_token_alloc(int64_t n);
+
+/* Tile sizes of the attention kernel for a recipe / head dim: BM queries per
+ * workgroup (128), BN keys per online-softmax step (64).  The online softmax visits key
+ * tiles of BN keys in ascending order and requantises P against the running
+ * maximum including the current tile, so BN is part of the result's
+ * definition (the reference oracle takes it as a parameter).
+ * mode: 0 dense, 1 causal, 2 sliding-tile. */
+pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, int* BN);
+
+/*
+ * pab_quantize - quantise one tensor with one recipe [FPS §2.1, §3.1; FP4G §1].
+ *
+ * x        device, logical [B, H, N_in, d] of in_dt with element strides
+ *          `strides` (any non-negative strides; the innermost must be 1).
+ * perm     device int32 [n_out] or NULL.  If given, kernel token p takes input
+ *          token perm[p] (a value of -1 gives a zero token: padding).  This is
+ *          the block transpose of [FPS §3.3 item 1] that makes each 3D tile
+ *          contiguous.  If NULL, n_out must equal N_in and token p is input
+ *          token p.
+ * block_tokens  tokens per scale block for PAB_FP8_TOKEN_BLOCK (a multiple of
+ *          16, at most 1024); ignored otherwise.
+ * Outputs (n_alloc = pab_token_alloc(n_out)):
+ *  PAB_FP8_TOKEN_BLOCK: codes uint8 [B, H, n_alloc, d];
+ *                       scales float32 [B, H, ceil(n_alloc / block_tokens)]
+ *                       (blocks holding no token below n_out get scale 1);
+ *                       operand (if not NULL) bfloat16 [B, H, n_alloc, d]: the
+ *                       exact value decode(code) of every code (not divided by
+ *                       the scale) - the attention kernel multiplies Q and K
+ *                       in this form, see pab_attention_dense.
+ *  PAB_FP8_CHANNEL:     codes uint8 [B, H, d, n_alloc] - transposed, and inside
+ *                       every 64-token group the token t = 32a + 8b + 4g + c
+ *                       (a < 2, b < 4, g < 2, c < 4) is stored at position
+ *                       32g + 16a + 4b + c (the operand order of the kernel's
+ *                       P.V product); scales float32 [B, H, d].
+ *  PAB_MXFP4_D32:       codes uint8 [B, H, n_alloc, d/2], two E2M1 codes per
+ *                       byte, channel 2k in the low nibble;
+ *                       scales uint8 (E8M0) [B, H, n_alloc, d/32].
+ * `operand` must be NULL for the other recipes.  x must be 16-byte aligned
+ * and the batch/head/token strides multiples of 8.
+ * d must be 64 or 128 (128 for MXFP4).  Inputs are assumed finite.
+ */
+pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
+                        const int64_t strides[4], pab_recipe recipe, int block_tokens,
+                        const int32_t* perm, int64_t n_out, void* codes, void* scales,
+                        void* operand, void* stream);
+
+/* A quantised operand as pab_quantize wrote it (all device pointers). */
+typedef struct {
+  const void* codes;
+  const void* scales;
+  const void* operand;   /* PAB_FP8_TOKEN_BLOCK: the bf16 operand copy (required) */
+  pab_recipe recipe;
+  int block_tokens;      /* PAB_FP8_TOKEN_BLOCK only */
+  int64_t B, H, N, d;    /* N = tokens (n_out of pab_quantize) */
+} pab_qview;
+
+/*
+ * pab_attention_dense - O = softmax(Q K^T * sm_scale) V, FlashAttention-style
+ * [FV §2.1; FA4 FlashAttention section], on quantised operands:
+ *  Q, K: PAB_FP8_TOKEN_BLOCK or PAB_MXFP4_D32 (both the same recipe);
+ *  V:    PAB_FP8_CHANNEL;
+ *  P:    requantised to FP8 E4M3 with the fixed per-tensor scale 1/448
+ *        [FPS §3.1]: P~ = E4M3(448 P) against the running row maximum.
+ * For each query row the kernel visits key tiles of BN keys in ascending
+ * order (causal: keys j <= i, top-left aligned) and keeps the running max m,
+ * the sum l of the unquantised P and the accumulator of P~ V in fp32.
+ * Q K^T of the FP8 recipe is summed from the exact products of the decoded
+ * E4M3 values (the bf16 operand copies) with fp32 accumulation; P~ V uses the
+ * FP8 matrix instructions.
+ * O[i,c] = acc[i,c] / (448 l_i) / s_V[c]; a row with no valid key gives 0.
+ * sm_scale <= 0 means 1/sqrt(d)  [FV §5.2 scaling_factor].
+ * kv_valid  device uint8 [N] or NULL: keys with 0 are masked (padding).
+ * out_perm  device int32 [N] or NULL: query p is stored at output token
+ *           out_perm[p] (skipped if -1); NULL stores query p at token p.
+ * out       device float32 [B, H, n_out_tokens, d] with element strides
+ *           out_strides (innermost 1); rows that no query maps to are not
+ *           written.
+ */
+pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                               int causal, float sm_scale, const uint8_t* kv_valid,
+                               const int32_t* out_perm, int64_t n_out_tokens, float* out,
+                               const int64_t out_strides[4], void* stream);
+
+/*
+ * pab_attention_sta - sliding-tile sparse attention [FPS §2.2]: the N tokens
+ * (kernel order, see pab_sta_plan) form n_tiles tiles of tile_tokens tokens;
+ * query tile u attends only to the key tiles win_idx[win_off[u] ..
+ * win_off[u+1]-1] (ascending), each visited as tile_tokens/BN key tiles in
+ * ascending order.  Everything else is as in pab_attention_dense (no causal
+ * mask).  A window list holding every tile gives the dense result bit for bit.
+ * win_off int32 [n_tiles+1], win_idx int32 [win_off[n_tiles]], tile_order
+ * int32 [n_tiles] (a permutation of the tiles: the order work is issued, e.g.
+ * longest window first [FA4, LPT scheduling]) - device pointers.
+ * tile_tokens must be a multiple of PAB_TOKEN_ALIGN and N == n_tiles *
+ * tile_tokens.
+ */
+pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                             float sm_scale, const int32_t* win_off, const int32_t* win_idx,
+                             const int32_t* tile_order, int n_tiles, int tile_tokens,
+                             const uint8_t* kv_valid, const int32_t* out_perm,
+                             int64_t n_out_tokens, float* out, const int64_t out_strides[4],
+                             void* stream);
+
+/*
+ * pab_sta_plan - host-side planner for sliding-tile attention [FPS §2.2,
+ * §3.3 item 1].  grid = (T, H, W) of the padded latent grid (each a multiple
+ * of tile), real_grid <= grid the unpadded grid whose tokens the caller holds
+ * in raster order, tile = (t, h, w) tokens per tile, window = (w_t, w_h, w_w)
+ * in tiles: key tile v is in the window of query tile u iff
+ * |u_a - v_a| <= floor(w_a / 2) on every axis, clipped at the grid border.
+ * Kernel token order: tiles in raster order over the tile grid, tokens in
+ * raster order inside a tile.
+ * Outputs (host memory; pass NULL to skip an array; call once with all NULL
+ * to get the sizes):
+ *   perm       int32 [n_tokens]: raster index in real_grid of kernel token p,
+ *              -1 for padding;
+ *   inv_perm   int32 [T_r*H_r*W_r]: kernel position of each real token;
+ *   kv_valid   uint8 [n_tokens]: 1 where perm >= 0;
+ *   win_off    int32 [n_tiles+1], win_idx int32 [n_pairs]: window lists,
+ *              ascending within each tile;
+ *   lpt_order  int32 [n_tiles]: tiles by decreasing window size, ties by
+ *              index.
+ * Pure host code, deterministic.
+ */
+pab_status pab_sta_plan(const int grid[3], const int real_grid[3], const int tile[3],
+                        const int window[3], int32_t* perm, int32_t* inv_perm,
+                        uint8_t* kv_valid, int32_t* win_off, int32_t* win_idx,
+                        int32_t* lpt_order, int64_t* n_tokens, int64_t* n_tiles,
+                        int64_t* n_pairs);
+
+/*
+ * pab_count_nonfinite - adds the number of NaN/Inf values among x[0..n) to
+ * *dev_count (device int32; the caller zeroes it).  Lets a caller fall back
+ * to another attention path when an output is not finite [FV §8.2].
+ */
+pab_status pab_count_nonfinite(const float* x, int64_t n, int32_t* dev_count, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAB_H */

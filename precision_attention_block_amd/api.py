@@ -1,0 +1,45 @@
+"""One-call attention on unquantised inputs: quantise Q, K, V with the staged
+recipe and run the fused kernel (all on the device through libpab).
+
+The FastVideo FP4 article (wmrh.cn, §5.2) calls its kernel as
+fp4_attention(qkv, mask, head_dim, scaling_factor); its §8.2 falls back to
+standard attention when the output holds NaN/Inf.  `check_finite=True` runs
+the library's non-finite count and raises, so that the caller can fall back;
+this module itself never computes attention another way."""
+from . import binding as B
+
+
+def quantize_qkv(q, k, v, recipe="fp8", block_tokens=128, perm=None, n_out=None):
+    if recipe == "fp8":
+        qq = B.quantize(q, "fp8_block", block_tokens, perm, n_out)
+        kq = B.quantize(k, "fp8_block", block_tokens, perm, n_out)
+    elif recipe == "mxfp4":
+        qq = B.quantize(q, "mxfp4", None, perm, n_out)
+        kq = B.quantize(k, "mxfp4", None, perm, n_out)
+    else:
+        raise ValueError(recipe)
+    vq = B.quantize(v, "fp8_channel", None, perm, n_out)
+    return qq, kq, vq
+
+
+def attention(q, k, v, recipe="fp8", block_tokens=128, causal=False, sm_scale=None, sta=None,
+              check_finite=False):
+    """q, k, v: CUDA tensors [B, H, N, d] (float32 or bfloat16, any strides with
+    unit channel stride; a packed qkv [B, N, 3, H, d] can be passed as three
+    permuted views).  sta: None, or a binding.DevicePlan for sliding-tile
+    attention over tokens given in raster order of the plan's real grid.
+    Returns float32 [B, H, N, d]."""
+    if sta is None:
+        qq, kq, vq = quantize_qkv(q, k, v, recipe, block_tokens)
+        out = B.attention_dense(qq, kq, vq, causal=causal, sm_scale=sm_scale)
+    else:
+        if causal:
+            raise ValueError("sliding-tile attention has no causal mask")
+        qq, kq, vq = quantize_qkv(q, k, v, recipe, sta.tile_tokens if block_tokens is None
+                                  else block_tokens, sta.perm, sta.n_tokens)
+        out = B.attention_sta(qq, kq, vq, sta, sm_scale=sm_scale)
+    if check_finite:
+        bad = int(B.count_nonfinite(out).item())
+        if bad:
+            raise FloatingPointError("attention output holds %d non-finite values" % bad)
+    return out

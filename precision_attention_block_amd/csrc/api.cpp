@@ -1,0 +1,331 @@
+// libpab C ABI: argument validation, launch configuration and the host-side
+// sliding-tile planner.  Every check runs before the first HIP call, so a call
+// rejected here has touched neither the device nor the stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+#include <algorithm>
+#include <numeric>
+
+#include "../../include/pab.h"
+#include "pab_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+pab_status hip_status(hipError_t e, hipStream_t st) {
+  if (e == hipSuccess) {
+    const char* dbg = std::getenv("PAB_SYNC_DEBUG");
+    if (dbg && dbg[0] == '1') {
+      e = hipStreamSynchronize(st);
+      if (e == hipSuccess) e = hipGetLastError();
+    }
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return PAB_HIP_ERROR;
+  }
+  return PAB_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t round_up(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
+
+// Validates a quantised operand view; `role` 0 = Q/K, 1 = V.
+pab_status check_view(const pab_qview* v, int role) {
+  if (!v || !v->codes || !v->scales) return PAB_INVALID_ARG;
+  if (v->B < 1 || v->H < 1 || v->N < 1 || v->d < 1) return PAB_INVALID_ARG;
+  if (v->B * v->H > (int64_t)1 << 24 || v->N > (int64_t)1 << 28) return PAB_UNSUPPORTED;
+  if (!aligned(v->codes, 16)) return PAB_INVALID_ARG;
+  if (role == 1) {
+    if (v->recipe != PAB_FP8_CHANNEL) return PAB_INVALID_ARG;
+    if (v->d != 64 && v->d != 128) return PAB_UNSUPPORTED;
+    return PAB_OK;
+  }
+  if (v->recipe == PAB_FP8_TOKEN_BLOCK) {
+    if (v->d != 64 && v->d != 128) return PAB_UNSUPPORTED;
+    if (v->block_tokens < 16 || v->block_tokens > 1024 || v->block_tokens % 16) return PAB_INVALID_ARG;
+    if (!v->operand || !aligned(v->operand, 16)) return PAB_INVALID_ARG;
+    return PAB_OK;
+  }
+  if (v->recipe == PAB_MXFP4_D32) return v->d == 128 ? PAB_OK : PAB_UNSUPPORTED;
+  return PAB_INVALID_ARG;
+}
+
+pab_status fill_attn_args(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                          float sm_scale, const uint8_t* kv_valid, const int32_t* out_perm,
+                          int64_t n_out_tokens, float* out, const int64_t out_strides[4],
+                          pab::AttnArgs& a) {
+  pab_status s;
+  if ((s = check_view(q, 0)) != PAB_OK) return s;
+  if ((s = check_view(k, 0)) != PAB_OK) return s;
+  if ((s = check_view(v, 1)) != PAB_OK) return s;
+  if (q->recipe != k->recipe) return PAB_INVALID_ARG;
+  if (q->B != k->B || q->B != v->B || q->H != k->H || q->H != v->H || q->N != k->N ||
+      q->N != v->N || q->d != k->d || q->d != v->d)
+    return PAB_INVALID_ARG;
+  if (!out || !out_strides) return PAB_INVALID_ARG;
+  if (out_strides[3] != 1 || out_strides[0] < 0 || out_strides[1] < 0 || out_strides[2] < 0)
+    return PAB_INVALID_ARG;
+  if (out_strides[0] % 4 || out_strides[1] % 4 || out_strides[2] % 4 || !aligned(out, 16))
+    return PAB_INVALID_ARG;
+  if (n_out_tokens < 1) return PAB_INVALID_ARG;
+  if (!out_perm && n_out_tokens < q->N) return PAB_INVALID_ARG;
+  if (kv_valid && !aligned(kv_valid, 4)) return PAB_INVALID_ARG;
+  if (!(std::isfinite(sm_scale))) return PAB_INVALID_ARG;
+  const bool mx = q->recipe == PAB_MXFP4_D32;
+  const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt((float)q->d);
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint8_t*>(q->codes);
+  a.k = static_cast<const uint8_t*>(k->codes);
+  a.q16 = static_cast<const uint8_t*>(q->operand);
+  a.k16 = static_cast<const uint8_t*>(k->operand);
+  a.vt = static_cast<const uint8_t*>(v->codes);
+  if (mx) {
+    a.q_mx = static_cast<const uint8_t*>(q->scales);
+    a.k_mx = static_cast<const uint8_t*>(k->scales);
+  } else {
+    a.q_scale = static_cast<const float*>(q->scales);
+    a.k_scale = static_cast<const float*>(k->scales);
+    a.blk_q = q->block_tokens;
+    a.blk_k = k->block_tokens;
+  }
+  a.v_scale = static_cast<const float*>(v->scales);
+  a.kv_valid = kv_valid;
+  a.out_perm = out_perm;
+  a.out = out;
+  a.osb = out_strides[0];
+  a.osh = out_strides[1];
+  a.osn = out_strides[2];
+  a.B = (int)q->B;
+  a.H = (int)q->H;
+  a.N = (int)q->N;
+  a.n_alloc = (int)round_up(q->N, PAB_TOKEN_ALIGN);
+  if (!mx) {
+    a.nblk_q = (int)((a.n_alloc + a.blk_q - 1) / a.blk_q);
+    a.nblk_k = (int)((a.n_alloc + a.blk_k - 1) / a.blk_k);
+  }
+  a.sm_log2 = scale * 1.4426950408889634f;
+  a.n_qtiles = a.n_alloc / pab::kBM;
+  return PAB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pab_abi_version(void) { return PAB_ABI_VERSION; }
+
+const char* pab_status_str(pab_status s) {
+  switch (s) {
+    case PAB_OK: return "ok";
+    case PAB_INVALID_ARG: return "invalid argument";
+    case PAB_UNSUPPORTED: return "unsupported configuration";
+    case PAB_HIP_ERROR: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int pab_last_hip_error(void) { return g_last_hip_error; }
+
+int64_t pab_token_alloc(int64_t n) { return n <= 0 ? 0 : round_up(n, PAB_TOKEN_ALIGN); }
+
+pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, int* BN) {
+  if (!BM || !BN) return PAB_INVALID_ARG;
+  if (mode < 0 || mode > 2) return PAB_INVALID_ARG;
+  if (qk_recipe == PAB_FP8_TOKEN_BLOCK) {
+    if (d != 64 && d != 128) return PAB_UNSUPPORTED;
+  } else if (qk_recipe == PAB_MXFP4_D32) {
+    if (d != 128) return PAB_UNSUPPORTED;
+  } else {
+    return PAB_INVALID_ARG;
+  }
+  *BM = pab::kBM;
+  *BN = pab::kBN;
+  return PAB_OK;
+}
+
+pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
+                        const int64_t strides[4], pab_recipe recipe, int block_tokens,
+                        const int32_t* perm, int64_t n_out, void* codes, void* scales,
+                        void* operand, void* stream) {
+  if (!x || !shape || !strides || !codes || !scales) return PAB_INVALID_ARG;
+  if (operand && (recipe != PAB_FP8_TOKEN_BLOCK || !aligned(operand, 16))) return PAB_INVALID_ARG;
+  if (in_dt != PAB_F32 && in_dt != PAB_BF16) return PAB_INVALID_ARG;
+  const int64_t B = shape[0], H = shape[1], N = shape[2], d = shape[3];
+  if (B < 1 || H < 1 || N < 1 || d < 1) return PAB_INVALID_ARG;
+  if (strides[3] != 1) return PAB_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (strides[i] < 0 || strides[i] % 8) return PAB_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return PAB_INVALID_ARG;
+  if (n_out < 1) return PAB_INVALID_ARG;
+  if (!perm && n_out != N) return PAB_INVALID_ARG;
+  if (B * H > (int64_t)1 << 24 || n_out > (int64_t)1 << 28 || N > (int64_t)1 << 31) return PAB_UNSUPPORTED;
+  if (recipe == PAB_FP8_TOKEN_BLOCK) {
+    if (d != 64 && d != 128) return PAB_UNSUPPORTED;
+    if (block_tokens < 16 || block_tokens > 1024 || block_tokens % 16) return PAB_INVALID_ARG;
+  } else if (recipe == PAB_FP8_CHANNEL) {
+    if (d != 64 && d != 128) return PAB_UNSUPPORTED;
+  } else if (recipe == PAB_MXFP4_D32) {
+    if (d != 128) return PAB_UNSUPPORTED;
+  } else {
+    return PAB_INVALID_ARG;
+  }
+  pab::QuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.sb = strides[0];
+  a.sh = strides[1];
+  a.sn = strides[2];
+  a.B = (int)B;
+  a.H = (int)H;
+  a.N_in = (int)N;
+  a.d = (int)d;
+  a.recipe = (int)recipe;
+  a.in_bf16 = in_dt == PAB_BF16;
+  a.perm = perm;
+  a.n_out = (int)n_out;
+  a.n_alloc = (int)round_up(n_out, PAB_TOKEN_ALIGN);
+  a.codes = static_cast<uint8_t*>(codes);
+  a.values = static_cast<uint16_t*>(operand);
+  if (recipe == PAB_MXFP4_D32) {
+    a.scales_u8 = static_cast<uint8_t*>(scales);
+  } else {
+    a.scales_f32 = static_cast<float*>(scales);
+  }
+  if (recipe == PAB_FP8_TOKEN_BLOCK) {
+    a.blk = block_tokens;
+    a.nblk = (int)((a.n_alloc + block_tokens - 1) / block_tokens);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(pab::launch_quantize(a, st), st);
+}
+
+pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                               int causal, float sm_scale, const uint8_t* kv_valid,
+                               const int32_t* out_perm, int64_t n_out_tokens, float* out,
+                               const int64_t out_strides[4], void* stream) {
+  pab::AttnArgs a;
+  pab_status s = fill_attn_args(q, k, v, sm_scale, kv_valid, out_perm, n_out_tokens, out,
+                                out_strides, a);
+  if (s != PAB_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32,
+                                          causal ? 1 : 0, st),
+                    st);
+}
+
+pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                             float sm_scale, const int32_t* win_off, const int32_t* win_idx,
+                             const int32_t* tile_order, int n_tiles, int tile_tokens,
+                             const uint8_t* kv_valid, const int32_t* out_perm,
+                             int64_t n_out_tokens, float* out, const int64_t out_strides[4],
+                             void* stream) {
+  if (!win_off || !win_idx || !tile_order) return PAB_INVALID_ARG;
+  if (n_tiles < 1 || tile_tokens < PAB_TOKEN_ALIGN || tile_tokens % PAB_TOKEN_ALIGN)
+    return PAB_INVALID_ARG;
+  pab::AttnArgs a;
+  pab_status s = fill_attn_args(q, k, v, sm_scale, kv_valid, out_perm, n_out_tokens, out,
+                                out_strides, a);
+  if (s != PAB_OK) return s;
+  if ((int64_t)n_tiles * tile_tokens != q->N) return PAB_INVALID_ARG;
+  a.win_off = win_off;
+  a.win_idx = win_idx;
+  a.tile_order = tile_order;
+  a.n_tiles = n_tiles;
+  a.tile_tokens = tile_tokens;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32, 2, st), st);
+}
+
+pab_status pab_sta_plan(const int grid[3], const int real_grid[3], const int tile[3],
+                        const int window[3], int32_t* perm, int32_t* inv_perm,
+                        uint8_t* kv_valid, int32_t* win_off, int32_t* win_idx,
+                        int32_t* lpt_order, int64_t* n_tokens, int64_t* n_tiles,
+                        int64_t* n_pairs) {
+  if (!grid || !real_grid || !tile || !window) return PAB_INVALID_ARG;
+  int nt[3], rad[3];
+  int64_t tokens = 1, tiles = 1, real = 1;
+  for (int i = 0; i < 3; ++i) {
+    if (grid[i] < 1 || tile[i] < 1 || real_grid[i] < 1 || window[i] < 1) return PAB_INVALID_ARG;
+    if (grid[i] % tile[i] || real_grid[i] > grid[i]) return PAB_INVALID_ARG;
+    nt[i] = grid[i] / tile[i];
+    rad[i] = window[i] / 2;
+    tokens *= grid[i];
+    tiles *= nt[i];
+    real *= real_grid[i];
+  }
+  if (tokens > (int64_t)1 << 30) return PAB_UNSUPPORTED;
+  // window size per tile: product over axes of the clipped interval length
+  auto axis_count = [&](int a, int c) {
+    return std::min(c + rad[a], nt[a] - 1) - std::max(c - rad[a], 0) + 1;
+  };
+  int64_t pairs = 0;
+  for (int ut = 0; ut < nt[0]; ++ut)
+    for (int uh = 0; uh < nt[1]; ++uh)
+      for (int uw = 0; uw < nt[2]; ++uw)
+        pairs += (int64_t)axis_count(0, ut) * axis_count(1, uh) * axis_count(2, uw);
+  if (n_tokens) *n_tokens = tokens;
+  if (n_tiles) *n_tiles = tiles;
+  if (n_pairs) *n_pairs = pairs;
+
+  if (perm || inv_perm || kv_valid) {
+    int64_t p = 0;
+    for (int ut = 0; ut < nt[0]; ++ut)
+      for (int uh = 0; uh < nt[1]; ++uh)
+        for (int uw = 0; uw < nt[2]; ++uw)
+          for (int dt = 0; dt < tile[0]; ++dt)
+            for (int dh = 0; dh < tile[1]; ++dh)
+              for (int dw = 0; dw < tile[2]; ++dw, ++p) {
+                const int t = ut * tile[0] + dt, h = uh * tile[1] + dh, w = uw * tile[2] + dw;
+                const bool ok = t < real_grid[0] && h < real_grid[1] && w < real_grid[2];
+                const int64_t r = ok ? ((int64_t)t * real_grid[1] + h) * real_grid[2] + w : -1;
+                if (perm) perm[p] = (int32_t)r;
+                if (kv_valid) kv_valid[p] = ok ? 1 : 0;
+                if (inv_perm && ok) inv_perm[r] = (int32_t)p;
+              }
+  }
+  if (win_off || win_idx || lpt_order) {
+    std::vector<int32_t> sizes(tiles);
+    int64_t pos = 0, u = 0;
+    if (win_off) win_off[0] = 0;
+    for (int ut = 0; ut < nt[0]; ++ut)
+      for (int uh = 0; uh < nt[1]; ++uh)
+        for (int uw = 0; uw < nt[2]; ++uw, ++u) {
+          const int t0 = std::max(ut - rad[0], 0), t1 = std::min(ut + rad[0], nt[0] - 1);
+          const int h0 = std::max(uh - rad[1], 0), h1 = std::min(uh + rad[1], nt[1] - 1);
+          const int w0 = std::max(uw - rad[2], 0), w1 = std::min(uw + rad[2], nt[2] - 1);
+          for (int vt = t0; vt <= t1; ++vt)
+            for (int vh = h0; vh <= h1; ++vh)
+              for (int vw = w0; vw <= w1; ++vw) {
+                if (win_idx) win_idx[pos] = (int32_t)(((int64_t)vt * nt[1] + vh) * nt[2] + vw);
+                ++pos;
+              }
+          sizes[u] = (t1 - t0 + 1) * (h1 - h0 + 1) * (w1 - w0 + 1);
+          if (win_off) win_off[u + 1] = (int32_t)pos;
+        }
+    if (lpt_order) {
+      std::vector<int32_t> order(tiles);
+      std::iota(order.begin(), order.end(), 0);
+      std::stable_sort(order.begin(), order.end(),
+                       [&](int32_t x, int32_t y) { return sizes[x] > sizes[y]; });
+      std::copy(order.begin(), order.end(), lpt_order);
+    }
+  }
+  return PAB_OK;
+}
+
+pab_status pab_count_nonfinite(const float* x, int64_t n, int32_t* dev_count, void* stream) {
+  if (!x || !dev_count || n < 0) return PAB_INVALID_ARG;
+  if (n == 0) return PAB_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(pab::launch_count_nonfinite(x, n, dev_count, st), st);
+}
+
+}  // extern "C"

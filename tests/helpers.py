@@ -1,0 +1,63 @@
+"""Shared test helpers: layout conversions of the library's documented output
+layouts, tolerances, and oracle runs on host copies of the inputs."""
+import numpy as np
+
+from oracle import attention as OA
+from oracle import quant as OQ
+from oracle import sta as OS
+
+# Attention parity gate (fp32 accumulate): max-abs and mean-abs error.
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+
+
+def _pos_of_token():
+    """Position inside a 64-token group of the transposed V codes for token t
+    (t = 32a + 8b + 4g + c is stored at 32g + 16a + 4b + c)."""
+    t = np.arange(64)
+    a, b, g, c = t // 32, (t % 32) // 8, (t % 8) // 4, t % 4
+    return 32 * g + 16 * a + 4 * b + c
+
+
+POS = _pos_of_token()
+
+
+def vt_to_tokens(vt, n):
+    """[..., d, n_alloc] transposed V codes -> [..., n, d] in token order."""
+    na = vt.shape[-1]
+    idx = (np.arange(na) // 64) * 64 + POS[np.arange(na) % 64]
+    tok = vt[..., idx]                       # [..., d, na] in token order
+    return np.swapaxes(tok, -1, -2)[..., :n, :]
+
+
+def oracle_operands(q, k, v, recipe, blk):
+    """Oracle quantisation of one (b, h) slice each: returns per-(b,h) Operand
+    triples as a nested list [B][H]."""
+    B, H = q.shape[:2]
+    out = [[None] * H for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            if recipe == "fp8":
+                qc, qs = OQ.fp8_block_quantize(q[b, h], blk)
+                kc, ks = OQ.fp8_block_quantize(k[b, h], blk)
+                qo = OA.Operand("fp8_block", qc, qs, blk)
+                ko = OA.Operand("fp8_block", kc, ks, blk)
+            else:
+                qc, qe = OQ.mxfp4_quantize(q[b, h])
+                kc, ke = OQ.mxfp4_quantize(k[b, h])
+                qo, ko = OA.Operand("mxfp4", qc, qe), OA.Operand("mxfp4", kc, ke)
+            vc, vs = OQ.fp8_channel_quantize(v[b, h])
+            out[b][h] = (qo, ko, OA.Operand("fp8_channel", vc, vs))
+    return out
+
+
+def compare(got, ref):
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    return float(err.max()), float(err.mean())
+
+
+def assert_close(got, ref, what=""):
+    mx, mean = compare(got, ref)
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, "%s: max-abs %.3g mean-abs %.3g" % (what, mx, mean)
+    return mx, mean

@@ -1,0 +1,151 @@
+"""GPU parity of the fused attention kernel against the oracle recipe at the
+kernel's KV tile size, through the C ABI: small shapes spanning several tiles
+and ragged tails, causal, MXFP4, key padding, output permutation and
+sliding-tile windows."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA
+from oracle import sta as OS
+from tests.helpers import assert_close, oracle_operands
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, H, N, d, seed, dtype=torch.bfloat16, outliers=True, scale=1.0):
+    rng = np.random.default_rng(seed)
+    qkv = [(rng.standard_normal((B, H, N, d)) * scale).astype(np.float32) for _ in range(3)]
+    if outliers:
+        for h in range(H):
+            ch = rng.permutation(d)[:4]
+            for t in range(2):
+                qkv[t][:, h, :, ch] *= rng.lognormal(0, 1.5, 4).astype(np.float32)[:, None, None]
+    ts = [torch.from_numpy(a).to(dtype) for a in qkv]
+    return [t.float().numpy() for t in ts], ts
+
+
+def _run_dense(lib, ts, recipe, blk, causal, sm_scale=None, kv_valid=None):
+    dev = [t.cuda() for t in ts]
+    if recipe == "fp8":
+        q = lib.quantize(dev[0], "fp8_block", blk)
+        k = lib.quantize(dev[1], "fp8_block", blk)
+    else:
+        q = lib.quantize(dev[0], "mxfp4")
+        k = lib.quantize(dev[1], "mxfp4")
+    v = lib.quantize(dev[2], "fp8_channel")
+    kvv = torch.from_numpy(kv_valid).cuda() if kv_valid is not None else None
+    out = lib.attention_dense(q, k, v, causal=causal, sm_scale=sm_scale, kv_valid=kvv)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _oracle_dense(x, recipe, blk, causal, sm_scale, bn, kv_valid=None, rows=None):
+    q, k, v = x
+    B, H, N, d = q.shape
+    ops = oracle_operands(q, k, v, recipe, blk)
+    out = np.zeros((B, H, N, d), np.float32)
+    rows = np.arange(N) if rows is None else rows
+    for b in range(B):
+        for h in range(H):
+            qo, ko, vo = ops[b][h]
+            out[b, h, rows] = OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm_scale, bn=bn,
+                                                  causal=causal, kv_valid=kv_valid)
+    return out
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=1, H=2, N=256, d=64, recipe="fp8", blk=64, causal=False, dtype=torch.float32, outl=False),
+    dict(B=1, H=2, N=1000, d=128, recipe="fp8", blk=128, causal=False, dtype=torch.bfloat16, outl=True),
+    dict(B=2, H=1, N=700, d=128, recipe="fp8", blk=128, causal=True, dtype=torch.bfloat16, outl=True),
+    dict(B=1, H=2, N=520, d=128, recipe="mxfp4", blk=None, causal=False, dtype=torch.bfloat16, outl=True),
+    dict(B=1, H=1, N=300, d=64, recipe="fp8", blk=32, causal=True, dtype=torch.float32, outl=False),
+    dict(B=1, H=2, N=384, d=128, recipe="fp8", blk=384, causal=False, dtype=torch.bfloat16, outl=True),
+], ids=["tiny_d64", "ragged_d128", "causal", "mxfp4", "causal_blk32_d64", "blk384"])
+def test_dense_parity(gpu_lib, case):
+    print("dense parity", case, flush=True)
+    x, ts = _inputs(case["B"], case["H"], case["N"], case["d"], 31 + case["N"], case["dtype"],
+                    case["outl"])
+    bm, bn = gpu_lib.attention_info("mxfp4" if case["recipe"] == "mxfp4" else "fp8_block",
+                                    case["d"], 1 if case["causal"] else 0)
+    sm = 1 / np.sqrt(case["d"])
+    got = _run_dense(gpu_lib, ts, case["recipe"], case["blk"], case["causal"])
+    ref = _oracle_dense(x, case["recipe"], case["blk"], case["causal"], sm, bn)
+    mx, mean = assert_close(got, ref, str(case))
+    print("  max-abs %.3g mean-abs %.3g" % (mx, mean))
+
+
+def test_key_padding_mask(gpu_lib):
+    x, ts = _inputs(1, 2, 600, 128, 5, torch.bfloat16, True)
+    valid = np.ones(600, np.uint8)
+    valid[[0, 1, 130, 131, 599]] = 0
+    valid[256:384] = 0                       # one whole key tile masked
+    got = _run_dense(gpu_lib, ts, "fp8", 128, False, kv_valid=valid)
+    ref = _oracle_dense(x, "fp8", 128, False, 1 / np.sqrt(128), 128, kv_valid=valid)
+    assert_close(got, ref, "kv_valid")
+
+
+def test_deterministic(gpu_lib):
+    _, ts = _inputs(1, 2, 900, 128, 6, torch.bfloat16, True)
+    a = _run_dense(gpu_lib, ts, "fp8", 128, False)
+    for _ in range(3):
+        assert np.array_equal(a, _run_dense(gpu_lib, ts, "fp8", 128, False))
+
+
+def _sta_setup(lib, grid, real, tile, window, H=2, seed=40, outl=True):
+    hp = lib.sta_plan(grid, real, tile, window)
+    op = OS.plan(grid, real, tile, window)
+    assert np.array_equal(hp.perm, op.perm) and np.array_equal(hp.win_idx, op.win_idx)
+    n_real = int(np.prod(real))
+    x, ts = _inputs(1, H, n_real, 128, seed, torch.bfloat16, outl)
+    return hp, op, x, ts
+
+
+def _run_sta(lib, hp, ts, window_plan=None, dense=False):
+    dp = lib.DevicePlan(hp if window_plan is None else window_plan)
+    dev = [t.cuda() for t in ts]
+    q = lib.quantize(dev[0], "fp8_block", hp.tile_tokens, perm=dp.perm, n_out=dp.n_tokens)
+    k = lib.quantize(dev[1], "fp8_block", hp.tile_tokens, perm=dp.perm, n_out=dp.n_tokens)
+    v = lib.quantize(dev[2], "fp8_channel", perm=dp.perm, n_out=dp.n_tokens)
+    if dense:
+        out = lib.attention_dense(q, k, v, kv_valid=dp.kv_valid, out_perm=dp.perm, n_out=dp.n_real)
+    else:
+        out = lib.attention_sta(q, k, v, dp)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("window", [(3, 3, 3), (1, 3, 5)])
+def test_sta_parity_with_padding(gpu_lib, window):
+    grid, real, tile = (6, 16, 32), (5, 15, 30), (2, 8, 8)
+    hp, op, x, ts = _sta_setup(gpu_lib, grid, real, tile, window)
+    got = _run_sta(gpu_lib, hp, ts)
+    _, bn = gpu_lib.attention_info("fp8_block", 128, 2)
+    xk = [OS.gather_tokens(a, op.perm) for a in x]
+    ops = oracle_operands(*xk, "fp8", op.tile_tokens)
+    ref = np.zeros_like(got)
+    tt = op.tile_tokens
+    for h in range(2):
+        qo, ko, vo = ops[0][h]
+        for u in range(op.n_tiles):
+            rows = np.arange(u * tt, (u + 1) * tt)
+            o = OA.recipe_attention(qo, ko, vo, rows, sm_scale=1 / np.sqrt(128), bn=bn,
+                                    kv_valid=op.kv_valid,
+                                    key_blocks=OS.key_blocks_for_tile(op, u, bn))
+            keep = op.perm[rows] >= 0
+            ref[0, h, op.perm[rows][keep]] = o[keep]
+    assert_close(got, ref, "sta %s" % (window,))
+
+
+def test_sta_full_window_equals_dense_bitwise(gpu_lib):
+    grid, real, tile = (4, 16, 16), (4, 13, 16), (2, 8, 8)
+    hp, op, x, ts = _sta_setup(gpu_lib, grid, real, tile, (9, 9, 9), seed=41)
+    sta = _run_sta(gpu_lib, hp, ts)
+    dense = _run_sta(gpu_lib, hp, ts, dense=True)
+    assert np.array_equal(sta, dense)
+
+
+def test_nonfinite_count(gpu_lib):
+    x = torch.zeros(1000, device="cuda")
+    x[[3, 500, 999]] = torch.tensor([float("nan"), float("inf"), -float("inf")], device="cuda")
+    assert int(gpu_lib.count_nonfinite(x).item()) == 3
