@@ -1,0 +1,257 @@
+"""Benchmark of the block-scaled attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+
+One step is one pass of the whole path over one batch of synthetic input
+already resident in HBM: quantise Q, K, V (FP8 per block or MXFP4 for Q/K, FP8
+per channel for V; for sliding-tile workloads with the fused 3D tile
+reorder) and run the fused attention kernel.  The sliding-tile plan is built
+once per shape on the host (it is a per-shape cost, like a compiled graph).
+
+Prints one JSON line: the metric is effective attention TFLOPS =
+algorithmic FLOPs / time, with FLOPs = 4 N^2 d H for dense attention (causal:
+4 d H N(N+1)/2; sliding-tile and padded grids: only real query-key pairs that
+are computed).  `value` uses the whole step (quantisers + attention);
+`roofline` is for the attention kernel alone, timed with events on the stream
+it runs on.  `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import CONFIGS, make_inputs, sample_rows  # noqa: E402
+
+DEFAULT_CONFIG = "dense_mxfp4_16k"
+# MI355X dense peaks (no sparsity), TFLOP/s
+PEAK_FP8 = 5000.0
+PEAK_FP4 = 10100.0
+PEAK_BF16 = 2500.0
+
+
+def algorithmic_flops(cfg, plan=None):
+    d, H, B = cfg.d, cfg.H, cfg.B
+    if cfg.mode == "sta":
+        real = plan.kv_valid.reshape(plan.n_tiles, plan.tile_tokens).sum(axis=1).astype(np.float64)
+        pairs = 0.0
+        for u in range(plan.n_tiles):
+            lst = plan.win_idx[plan.win_off[u]:plan.win_off[u + 1]]
+            pairs += real[u] * real[lst].sum()
+        return 4.0 * d * H * B * pairs
+    n = float(cfg.n_real)
+    if cfg.mode == "causal":
+        return 4.0 * d * H * B * n * (n + 1) / 2
+    return 4.0 * d * H * B * n * n
+
+
+def roofline_peak(cfg):
+    """Peak of the attention contraction for this recipe: MXFP4 QK^T + FP8 P.V
+    blend the FP4 and FP8 rates; the FP8 recipe is priced at the FP8 rate."""
+    if cfg.recipe == "mxfp4":
+        return 2.0 / (1.0 / PEAK_FP4 + 1.0 / PEAK_FP8)
+    return PEAK_FP8
+
+
+class GpuPath:
+    """Device tensors and one step of the path through the C ABI."""
+
+    def __init__(self, cfg, x, lib):
+        import torch
+        self.cfg, self.lib = cfg, lib
+        dev = torch.device("cuda:0")
+        self.q, self.k, self.v = (x[n].to(dev) for n in ("q_t", "k_t", "v_t"))
+        self.plan = None
+        self.dplan = None
+        if cfg.grid is not None:
+            self.plan = lib.sta_plan(cfg.grid, cfg.real_grid, cfg.tile,
+                                     cfg.window if cfg.window else (99, 99, 99))
+            self.dplan = lib.DevicePlan(self.plan, dev)
+        self.out = torch.empty((cfg.B, cfg.H, cfg.n_real, cfg.d), dtype=torch.float32, device=dev)
+
+    def quantize(self):
+        cfg, lib = self.cfg, self.lib
+        perm = self.dplan.perm if self.dplan is not None else None
+        n_out = cfg.n_kernel
+        if cfg.recipe == "fp8":
+            qq = lib.quantize(self.q, "fp8_block", cfg.blk, perm, n_out)
+            kq = lib.quantize(self.k, "fp8_block", cfg.blk, perm, n_out)
+        else:
+            qq = lib.quantize(self.q, "mxfp4", None, perm, n_out)
+            kq = lib.quantize(self.k, "mxfp4", None, perm, n_out)
+        vq = lib.quantize(self.v, "fp8_channel", None, perm, n_out)
+        return qq, kq, vq
+
+    def attend(self, qq, kq, vq):
+        cfg, lib = self.cfg, self.lib
+        if cfg.mode == "sta":
+            return lib.attention_sta(qq, kq, vq, self.dplan, out=self.out)
+        if self.dplan is not None:
+            return lib.attention_dense(qq, kq, vq, kv_valid=self.dplan.kv_valid,
+                                       out_perm=self.dplan.perm, n_out=cfg.n_real, out=self.out)
+        return lib.attention_dense(qq, kq, vq, causal=cfg.mode == "causal", out=self.out)
+
+
+def time_gpu(path, steps, warmup):
+    import torch
+    st = torch.cuda.current_stream()
+    for _ in range(warmup):
+        path.attend(*path.quantize())
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(st)
+        ops = path.quantize()
+        e1.record(st)
+        path.attend(*ops)
+        e2.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    a_ms = [b.elapsed_time(c) for _, b, c in ev]
+    return wall, q_ms, a_ms
+
+
+def cpu_baseline(cfg, x, plan, bn, budget_s=15.0):
+    """The oracle (as it stands) on a bounded sample: quantise one head's Q, K,
+    V and run the recipe for a set of query rows of that head; scaled to the
+    metric's unit with the same FLOP formula (computed query-key pairs)."""
+    from oracle import attention as OA
+    from oracle import quant as OQ
+    from oracle import sta as OS
+    cores = len(os.sched_getaffinity(0))
+    q, k, v = (x[n][0, 0] for n in ("q", "k", "v"))   # one (b, h) slice, raster order
+    t0 = time.perf_counter()
+    if plan is not None:
+        q, k, v = (OS.gather_tokens(a[None], plan.perm)[0] for a in (q, k, v))
+    if cfg.recipe == "fp8":
+        qc, qs = OQ.fp8_block_quantize(q, cfg.blk)
+        kc, ks = OQ.fp8_block_quantize(k, cfg.blk)
+        qo, ko = OA.Operand("fp8_block", qc, qs, cfg.blk), OA.Operand("fp8_block", kc, ks, cfg.blk)
+    else:
+        qc, qe = OQ.mxfp4_quantize(q)
+        kc, ke = OQ.mxfp4_quantize(k)
+        qo, ko = OA.Operand("mxfp4", qc, qe), OA.Operand("mxfp4", kc, ke)
+    vc, vs = OQ.fp8_channel_quantize(v)
+    vo = OA.Operand("fp8_channel", vc, vs)
+    t_quant = time.perf_counter() - t0
+    sm = 1.0 / np.sqrt(cfg.d)
+    n = q.shape[0]
+    kv_valid = plan.kv_valid if plan is not None else None
+    rows_done, pairs, t_att = 0, 0.0, 0.0
+    chunk = 64
+    rng = np.random.default_rng(1000 * cfg.index + 6)
+    while t_att < budget_s and rows_done < n:
+        if cfg.mode == "sta":
+            u = int(rng.integers(plan.n_tiles))
+            rows = np.arange(u * plan.tile_tokens, u * plan.tile_tokens + chunk)
+            kb = OS.key_blocks_for_tile(plan, u, bn)
+            t1 = time.perf_counter()
+            OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm, bn=bn, kv_valid=kv_valid, key_blocks=kb)
+            t_att += time.perf_counter() - t1
+            keys = plan.kv_valid[np.concatenate([np.arange(s, s + bn) for s in kb])].sum()
+            pairs += float((plan.kv_valid[rows] > 0).sum()) * keys
+        else:
+            r0 = int(rng.integers(0, max(1, n - chunk)))
+            rows = np.arange(r0, min(n, r0 + chunk))
+            t1 = time.perf_counter()
+            OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm, bn=bn, causal=cfg.mode == "causal",
+                                kv_valid=kv_valid)
+            t_att += time.perf_counter() - t1
+            if cfg.mode == "causal":
+                pairs += float((rows + 1).sum())
+            elif kv_valid is not None:
+                pairs += float((kv_valid[rows] > 0).sum()) * float(kv_valid.sum())
+            else:
+                pairs += float(len(rows)) * n
+        rows_done += len(rows)
+    tflops = 4.0 * cfg.d * pairs / t_att / 1e12
+    return {"value": tflops, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": "oracle recipe attention on %d query rows of one head (%.1f s; quantisation "
+                      "of that head's Q/K/V took %.1f s, not in the value)" % (rows_done, t_att, t_quant)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from precision_attention_block_amd import binding as lib
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib.lib()
+    cfg = CONFIGS[args.config]
+    print("[bench] config %s: generating inputs" % cfg.name, file=sys.stderr, flush=True)
+    x = make_inputs(cfg, as_torch=True)
+    path = GpuPath(cfg, x, lib)
+    mode = {"dense": 0, "causal": 1, "sta": 2}[cfg.mode]
+    _, bn = lib.attention_info("mxfp4" if cfg.recipe == "mxfp4" else "fp8_block", cfg.d, mode)
+    print("[bench] timing %d steps after %d warm-up" % (args.steps, args.warmup), file=sys.stderr,
+          flush=True)
+    wall, q_ms, a_ms = time_gpu(path, args.steps, args.warmup)
+    flops = algorithmic_flops(cfg, path.plan)
+    ms_step = wall * 1e3 / args.steps
+    att_ms = float(np.mean(a_ms))
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    peak = roofline_peak(cfg)
+    dense_equiv = 4.0 * cfg.d * cfg.H * cfg.B * float(cfg.n_real) ** 2
+    result = {
+        "metric": "effective attention TFLOPS (4*N^2*d*H) + % of FP8/MXFP4 MFMA peak, 1 GPU",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4+fp8" if cfg.recipe == "mxfp4" else "fp8",
+        "data": "synthetic (seeded N(0,1), bf16, outlier channels as configured)",
+        "config": {"workload": cfg.name, "desc": cfg.desc, "B": cfg.B, "H": cfg.H,
+                   "N": cfg.n_real, "N_kernel": cfg.n_kernel, "d": cfg.d, "mode": cfg.mode,
+                   "recipe": cfg.recipe, "block_tokens": cfg.blk if cfg.recipe == "fp8" else 32,
+                   "BN": bn, "algorithmic_flops": flops,
+                   "dense_equivalent_flops": dense_equiv,
+                   "quantize_ms": round(float(np.mean(q_ms)), 4),
+                   "attention_ms": round(att_ms, 4),
+                   "attention_ms_min_max": [round(min(a_ms), 4), round(max(a_ms), 4)],
+                   "attention_tflops": round(achieved, 2),
+                   "pct_fp8_peak": round(100 * achieved / PEAK_FP8, 2),
+                   "pct_fp4_peak": round(100 * achieved / PEAK_FP4, 2) if cfg.recipe == "mxfp4" else None},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+    }
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, x, path.plan and _oracle_plan(cfg), bn)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+def _oracle_plan(cfg):
+    from oracle import sta as OS
+    return OS.plan(cfg.grid, cfg.real_grid, cfg.tile, cfg.window if cfg.window else (99, 99, 99))
+
+
+if __name__ == "__main__":
+    main()

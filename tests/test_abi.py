@@ -1,0 +1,132 @@
+"""CPU tests of the C ABI library: it loads, exports every symbol the header
+declares, its planner matches the oracle planner, and argument validation
+rejects bad calls before touching a device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import sta as OS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from precision_attention_block_amd import binding
+    binding.lib()
+    return binding
+
+
+def test_exports_every_declared_symbol(B):
+    header = open(os.path.join(ROOT, "include", "pab.h")).read()
+    declared = set(re.findall(r"\b(pab_[a-z_]+)\s*\(", header))
+    assert declared == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(B.lib(), name), name
+    assert B.lib().pab_abi_version() == 1
+
+
+def test_token_alloc_and_info(B):
+    assert B.token_alloc(1) == 128 and B.token_alloc(128) == 128 and B.token_alloc(129) == 256
+    assert B.attention_info("fp8_block", 128, 0) == (128, 64)
+    assert B.attention_info("mxfp4", 128, 1)[1] == 64
+    with pytest.raises(B.PabError):
+        B.attention_info("mxfp4", 64, 0)
+    with pytest.raises(B.PabError):
+        B.attention_info("fp8_block", 96, 0)
+
+
+@pytest.mark.parametrize("grid,real,tile,window", [
+    ((12, 48, 80), (12, 48, 80), (6, 8, 8), (3, 3, 3)),
+    ((24, 48, 80), (21, 45, 80), (6, 8, 8), (3, 5, 5)),
+    ((4, 8, 8), (3, 7, 8), (2, 4, 4), (1, 3, 5)),
+    ((6, 16, 32), (5, 15, 30), (2, 8, 8), (9, 9, 9)),
+])
+def test_native_planner_matches_oracle(B, grid, real, tile, window):
+    hp = B.sta_plan(grid, real, tile, window)
+    op = OS.plan(grid, real, tile, window)
+    assert np.array_equal(hp.perm, op.perm)
+    assert np.array_equal(hp.kv_valid, op.kv_valid)
+    assert np.array_equal(hp.win_off, op.win_off)
+    assert np.array_equal(hp.win_idx, op.win_idx)
+    assert np.array_equal(hp.lpt, op.lpt)
+    ok = op.perm >= 0
+    assert np.array_equal(hp.inv_perm[op.perm[ok]], np.nonzero(ok)[0])
+
+
+def _st(B, name, *args):
+    return getattr(B.lib(), name)(*args)
+
+
+def test_quantize_validation_without_device(B):
+    L = B.lib()
+    shape = B._i64([1, 2, 256, 128])
+    strides = B._i64([2 * 256 * 128, 256 * 128, 128, 1])
+    fake = ctypes.c_void_p(4096)          # aligned, never dereferenced: validation fails first
+    null = ctypes.c_void_p(0)
+    q = lambda *a: L.pab_quantize(*a)
+    # null input / outputs
+    assert q(null, 1, shape, strides, 0, 128, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
+    assert q(fake, 1, shape, strides, 0, 128, null, 256, null, fake, fake, null) == B.PAB_INVALID_ARG
+    # bad dtype, recipe, block, n_out, strides, alignment, unsupported d
+    assert q(fake, 7, shape, strides, 0, 128, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
+    assert q(fake, 1, shape, strides, 9, 128, null, 256, fake, fake, null, null) == B.PAB_INVALID_ARG
+    assert q(fake, 1, shape, strides, 0, 100, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
+    assert q(fake, 1, shape, strides, 0, 2048, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
+    assert q(fake, 1, shape, strides, 0, 128, null, 300, fake, fake, fake, null) == B.PAB_INVALID_ARG
+    bad_str = B._i64([2 * 256 * 128, 256 * 128, 128, 2])
+    assert q(fake, 1, shape, bad_str, 0, 128, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
+    odd_str = B._i64([2 * 256 * 128, 256 * 128, 130, 1])
+    assert q(fake, 1, shape, odd_str, 0, 128, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
+    assert q(ctypes.c_void_p(4098), 1, shape, strides, 0, 128, null, 256, fake, fake, fake, null) \
+        == B.PAB_INVALID_ARG
+    shape96 = B._i64([1, 2, 256, 96])
+    assert q(fake, 1, shape96, strides, 0, 128, null, 256, fake, fake, fake, null) == B.PAB_UNSUPPORTED
+    shape64 = B._i64([1, 2, 256, 64])
+    assert q(fake, 1, shape64, strides, 2, 0, null, 256, fake, fake, null, null) == B.PAB_UNSUPPORTED
+    # an operand copy is only defined for the FP8 block recipe
+    assert q(fake, 1, shape, strides, 1, 0, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
+    assert L.pab_last_hip_error() == 0
+
+
+def test_attention_validation_without_device(B):
+    L = B.lib()
+    fake = 4096
+    mk = lambda recipe, n=256, d=128, blk=128, op=fake: B.QView(fake, fake, op, recipe, blk, 1, 2, n, d)
+    qv, kv, vv = mk(0), mk(0), mk(1)
+    out_str = B._i64([2 * 256 * 128, 256 * 128, 128, 1])
+    null = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(fake)
+    dense = lambda q, k, v, strides=out_str, n_out=256, sm=0.0: L.pab_attention_dense(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, sm, null, null, n_out, f, strides, null)
+    assert dense(qv, kv, mk(0)) == B.PAB_INVALID_ARG          # V with the Q/K recipe
+    assert dense(qv, mk(2), vv) == B.PAB_INVALID_ARG          # mixed Q/K recipes
+    assert dense(qv, mk(0, n=300), vv) == B.PAB_INVALID_ARG   # shape mismatch
+    assert dense(mk(0, op=0), kv, vv) == B.PAB_INVALID_ARG    # FP8 Q without operand copy
+    assert dense(mk(0, d=96), mk(0, d=96), mk(1, d=96)) == B.PAB_UNSUPPORTED
+    assert dense(qv, kv, vv, n_out=100) == B.PAB_INVALID_ARG  # output too small
+    assert dense(qv, kv, vv, sm=float("nan")) == B.PAB_INVALID_ARG
+    bad = B._i64([2 * 256 * 128, 256 * 128, 130, 1])
+    assert dense(qv, kv, vv, strides=bad) == B.PAB_INVALID_ARG
+    sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, f, f, f,
+                              2, 100, null, null, 256, f, out_str, null)
+    assert sta == B.PAB_INVALID_ARG                           # tile not a multiple of 128
+    sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, f, f, f,
+                              3, 128, null, null, 256, f, out_str, null)
+    assert sta == B.PAB_INVALID_ARG                           # tiles do not cover N
+    assert L.pab_last_hip_error() == 0
+
+
+def test_planner_validation(B):
+    L = B.lib()
+    c3 = lambda v: (ctypes.c_int * 3)(*v)
+    n = ctypes.c_int64()
+    assert L.pab_sta_plan(c3((12, 48, 80)), c3((12, 48, 80)), c3((5, 8, 8)), c3((3, 3, 3)),
+                          None, None, None, None, None, None, ctypes.byref(n), None, None) \
+        == B.PAB_INVALID_ARG                                  # grid not a multiple of tile
+    assert L.pab_sta_plan(c3((12, 48, 80)), c3((13, 48, 80)), c3((6, 8, 8)), c3((3, 3, 3)),
+                          None, None, None, None, None, None, ctypes.byref(n), None, None) \
+        == B.PAB_INVALID_ARG                                  # real grid larger than grid

@@ -81,7 +81,8 @@ def test_key_padding_mask(gpu_lib):
     valid[[0, 1, 130, 131, 599]] = 0
     valid[256:384] = 0                       # one whole key tile masked
     got = _run_dense(gpu_lib, ts, "fp8", 128, False, kv_valid=valid)
-    ref = _oracle_dense(x, "fp8", 128, False, 1 / np.sqrt(128), 128, kv_valid=valid)
+    _, bn = gpu_lib.attention_info("fp8_block", 128, 0)
+    ref = _oracle_dense(x, "fp8", 128, False, 1 / np.sqrt(128), bn, kv_valid=valid)
     assert_close(got, ref, "kv_valid")
 
 
