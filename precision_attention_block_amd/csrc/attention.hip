@@ -60,15 +60,21 @@ __device__ constexpr int swz(int row) {
 
 template <int D, bool MX>
 struct Tile {
-  // FP8 recipe: K as bf16 (exact E4M3 values); MXFP4: packed E2M1
+  // K ring stage: FP8 recipe: K as bf16 (exact E4M3 values); MXFP4: packed
+  // E2M1 plus the E8M0 group scales.
   static constexpr int KROW = MX ? D / 2 : 2 * D;   // bytes of one key row
   static constexpr int K_CPR = KROW / 16;
   static constexpr int K_BYTES = kBN * KROW;
-  static constexpr int V_BYTES = D * kBN;           // V^T: D rows of kBN E4M3 codes
   static constexpr int S_BYTES = MX ? kBN * (D / 32) : 0;
-  static constexpr int M_BYTES = kBN;                // key padding mask
-  static constexpr int BUF = K_BYTES + V_BYTES + S_BYTES + M_BYTES;
-  static_assert(BUF % 16 == 0, "LDS stages must stay 16-byte aligned");
+  static constexpr int KBUF = K_BYTES + S_BYTES;
+  // V ring stage: V^T codes, the key padding mask and (FP8) the K block scales
+  static constexpr int V_BYTES = D * kBN;           // D rows of kBN E4M3 codes
+  static constexpr int M_BYTES = kBN;
+  static constexpr int C_BYTES = MX ? 0 : 16;       // K block scales of the tile (<= 4)
+  static constexpr int VBUF = V_BYTES + M_BYTES + C_BYTES;
+  static constexpr int KI = K_BYTES / 1024 / 4;     // LDS-DMA instructions per wave
+  static constexpr int VI = V_BYTES / 1024 / 4;
+  static_assert(KBUF % 16 == 0 && VBUF % 16 == 0, "LDS stages must stay 16-byte aligned");
   static_assert(K_BYTES % 4096 == 0 && V_BYTES % 4096 == 0, "copy must split over 4 waves");
 };
 
@@ -94,42 +100,77 @@ struct DmaPlan {
 #if defined(__HIP_DEVICE_COMPILE__)
 // (buffer descriptors and everything that uses them exist in the device pass only)
 struct HeadBuffers {
-  __amdgpu_buffer_rsrc_t k, v, s, m;
+  __amdgpu_buffer_rsrc_t k, v, s, m, c;
   bool has_mask;
+  int blk_k;
 };
 constexpr int kRsrcWord3 = 0x00020000;   // raw byte buffer
 
-// Issues the asynchronous global->LDS copy of the key/value tile starting at
-// key `ks` into stage `lbuf` (4 waves share the instructions).  Reads past the
-// end of a buffer return zeros, so the padding mask reads as 0 = masked there.
-template <int D, bool MX, typename KPlan, typename VPlan>
-__device__ inline void issue_tile(uint8_t* lbuf, const HeadBuffers& hb, int n_alloc, int ks,
-                                  int wave, int lane, const KPlan& kp, const VPlan& vp) {
+// Every wave issues the same number of LDS-DMA instructions per stage (K for
+// a K stage, V for a V stage), and every pipeline iteration copies one K and
+// one V stage, so one outstanding-copy count serves every wave and iteration.
+template <int D, bool MX>
+struct Issues {
+  static constexpr int K = Tile<D, MX>::KI + (MX ? 1 : 0);
+  static constexpr int V = Tile<D, MX>::VI + 1 + (MX ? 0 : 1);
+};
+
+// Copies the K (and MXFP4 group scales) of the key tile at `ks` into a K stage.
+template <int D, bool MX, typename KPlan>
+__device__ inline void issue_k(uint8_t* kbuf, const HeadBuffers& hb, int ks, int wave, int lane,
+                               const KPlan& kp) {
   using TL = Tile<D, MX>;
-  constexpr int KI = TL::K_BYTES / 1024 / 4, VI = TL::V_BYTES / 1024 / 4;
   constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI, KPER = DmaPlan<TL::K_CPR>::PER;
 #pragma unroll
-  for (int j = 0; j < KI; ++j) {
-    const int inst = wave * KI + j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(lbuf + inst * 1024), 16,
+  for (int j = 0; j < TL::KI; ++j) {
+    const int inst = wave * TL::KI + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16,
                                              kp.off[inst % KPER], (ks + inst * KRPI) * TL::KROW, 0, 0);
   }
-#pragma unroll
-  for (int j = 0; j < VI; ++j) {
-    const int inst = wave * VI + j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.v, (lds_void_t*)(lbuf + TL::K_BYTES + inst * 1024), 16,
-                                             vp.off[0], ks + inst * 16 * n_alloc, 0, 0);
-  }
-  if (MX && wave == 3 && lane < TL::S_BYTES / 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(lbuf + TL::K_BYTES + TL::V_BYTES),
-                                             16, 16 * lane, ks * (D / 32), 0, 0);
-  if (hb.has_mask && wave == 2 && lane < TL::M_BYTES / 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        hb.m, (lds_void_t*)(lbuf + TL::K_BYTES + TL::V_BYTES + TL::S_BYTES), 16, 16 * lane, ks, 0, 0);
+  if (MX && lane < 4)   // 256 bytes of E8M0 scales: 4 lanes x 16 bytes per wave
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(kbuf + TL::K_BYTES + 64 * wave), 16,
+                                             16 * (lane & 3), ks * (D / 32) + 64 * wave, 0, 0);
 }
 
-// Waits for this wave's outstanding global->LDS copies.
-__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Copies V^T, the padding mask and (FP8) the K block scales of the key tile at
+// `ks` into a V stage.  Each LDS-DMA instruction writes 16 bytes per active
+// lane, so the small copies run on lane 0 only (every wave copies the same K
+// scales to the same place, which is harmless).
+template <int D, bool MX, typename VPlan>
+__device__ inline void issue_v(uint8_t* vbuf, const HeadBuffers& hb, int n_alloc, int ks, int wave,
+                               int lane, const VPlan& vp) {
+  using TL = Tile<D, MX>;
+#pragma unroll
+  for (int j = 0; j < TL::VI; ++j) {
+    const int inst = wave * TL::VI + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.v, (lds_void_t*)(vbuf + inst * 1024), 16, vp.off[0],
+                                             ks + inst * 16 * n_alloc, 0, 0);
+  }
+  if (lane == 0)   // 64 mask bytes, 16 per wave (zeros when there is no mask: ignored then)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.m, (lds_void_t*)(vbuf + TL::V_BYTES + 16 * wave), 16,
+                                             0, ks + 16 * wave, 0, 0);
+  if (!MX && lane == 0)   // the K block scales covering keys ks .. ks + BN - 1 (block size >= 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.c, (lds_void_t*)(vbuf + TL::V_BYTES + TL::M_BYTES),
+                                             16, 0, (ks / hb.blk_k) * 4, 0, 0);
+}
+
+// Workgroup barrier that does not wait for outstanding LDS-DMA copies (a
+// plain __syncthreads() fences every memory operation, including the copies
+// that are meant to stay in flight); this wave's LDS reads are complete first.
+// The waits use the s_waitcnt builtin (simm16: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8) rather than inline asm so that the compiler's own
+// wait-count tracking sees them and adds no conservative waits of its own.
+__device__ inline void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_s_barrier();
+}
+
+// Waits until at most N of this wave's LDS-DMA copies are outstanding.
+template <int N>
+__device__ inline void wait_vm_le() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 __device__ inline v8i make_v8(uint4 lo, uint4 hi) {
   v8i r;
@@ -142,7 +183,6 @@ __device__ inline v8i make_v8(uint4 lo, uint4 hi) {
 __device__ inline bool has_zero_byte(uint32_t w) {
   return ((w - 0x01010101u) & ~w & 0x80808080u) != 0u;
 }
-
 #endif  // __HIP_DEVICE_COMPILE__
 
 __device__ inline float swap_max(float v) {
@@ -156,19 +196,31 @@ __device__ inline float swap_sum(float v) {
 
 // MODE: 0 dense, 1 causal (top-left aligned), 2 sliding-tile.
 // UK: the K scale is constant over each key tile (FP8 blocks a multiple of BN).
+//
+// Software pipeline over key tiles t = 0, 1, ...: iteration t issues the
+// copies of K(t+3) and V(t+2), the QK^T MFMAs of tile t+1, the softmax of
+// tile t (interleaved with those MFMAs) and the P.V MFMAs of tile t.  K and
+// V each have a 3-stage LDS ring, so every copy has two iterations to land.
 template <int D, bool MX, int MODE, bool UK>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, (MX && MODE != 2) ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using TL = Tile<D, MX>;
   constexpr int DB = D / 32;            // 32-channel blocks of O^T
   constexpr int QI = D / 16;            // bf16 32x32x16 MFMAs over d (FP8 recipe)
-  // Two pipeline stages as two distinct LDS objects: the compiler can then see
-  // that the copy into one stage does not alias reads of the other and does
-  // not wait for the copy before those reads.
-  __shared__ __align__(16) uint8_t stage0[TL::BUF];
-  __shared__ __align__(16) uint8_t stage1[TL::BUF];
+  constexpr int NK = Issues<D, MX>::K, NV = Issues<D, MX>::V;
+  constexpr int QK_MFMA = MX ? 4 : 2 * QI;          // QK^T MFMAs per key tile
+  constexpr int VALU_PER_MFMA = MX ? 30 : 8;
+  constexpr int PRE_DS = 8;                          // LDS reads issued ahead
+  constexpr int DS_PER_MFMA = MX ? 2 : 1;
+  constexpr bool INTERLEAVE = true;
+  // Distinct LDS objects per stage: the compiler can then see that a copy
+  // into one stage does not alias reads of another and does not wait for it.
+  __shared__ __align__(16) uint8_t k0[TL::KBUF], k1[TL::KBUF], k2[TL::KBUF];
+  __shared__ __align__(16) uint8_t v0[TL::VBUF], v1[TL::VBUF], v2[TL::VBUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform; saying so keeps LDS-DMA addresses (M0) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;     // MFMA column (query) and k-group
   const int work = xcd_work_index(blockIdx.x, gridDim.x);
 
@@ -192,8 +244,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
   const int wq0 = q0 + wave * 32;             // first query of this wave
   const int myq = wq0 + lr;                   // this lane's query
+  const int32_t* wlist = MODE == 2 ? a.win_idx + a.win_off[u] : nullptr;
   auto step_start = [&](int t) -> int {
-    if (MODE == 2) return a.win_idx[a.win_off[u] + t / spt] * a.tile_tokens + (t % spt) * kBN;
+    if (MODE == 2) return wlist[t / spt] * a.tile_tokens + (t % spt) * kBN;
     return t * kBN;
   };
 
@@ -249,13 +302,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   hb.has_mask = a.kv_valid != nullptr;
   hb.m = __builtin_amdgcn_make_buffer_rsrc((void*)(hb.has_mask ? a.kv_valid : kbh), 0,
                                            hb.has_mask ? a.N : 0, kRsrcWord3);
-  issue_tile<D, MX>(stage0, hb, a.n_alloc, step_start(0), wave, lane, kp, vp);
-  wait_vm();
-  __syncthreads();
+  hb.blk_k = MX ? 1 : a.blk_k;
+  hb.c = __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? kbh : (const void*)(a.k_scale + (int64_t)bh * a.nblk_k)),
+                                           0, MX ? 0 : a.nblk_k * 4, kRsrcWord3);
 
   // Per-lane byte offsets of this lane's operand chunks inside a stage; the
-  // rows are 32 kb + lr, so the swizzle depends on lr only (the tile's row
-  // count per block, 32, is a multiple of every swizzle period).
+  // rows are 32 kb + lr, so the swizzle depends on lr only (32, the rows per
+  // block, is a multiple of every swizzle period).
   int k_off[MX ? 2 : QI];
   if (MX) {
 #pragma unroll
@@ -267,19 +320,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int v_off0 = lr * kBN + 16 * ((2 * lg) ^ swz<4>(lr));
   const int v_off1 = lr * kBN + 16 * ((2 * lg + 1) ^ swz<4>(lr));
 
-  auto step = [&](const int t, const uint8_t* Ks, uint8_t* next_stage) __attribute__((always_inline)) {
-    const int ks = step_start(t);
-    const bool more = t + 1 < n_steps;
-    const uint8_t* Vs = Ks + TL::K_BYTES;
-    const uint8_t* Ss = Vs + TL::V_BYTES;
-    const uint8_t* Ms = Ss + TL::S_BYTES;
-
-    // ---- start copying the next key/value tile into the other stage
-    if (more) issue_tile<D, MX>(next_stage, hb, a.n_alloc, step_start(t + 1), wave, lane, kp, vp);
-
-    // ---- S^T (keys x queries) for the two 32-key blocks, fp32 accumulate.
-    // s[kb][j] is key ks + 32 kb + 8 (j / 4) + 4 lg + j % 4 of query myq.
-    v16f s[2];
+  // S^T (keys x queries) of the key tile in K stage `Ks`, fp32 accumulate:
+  // s[kb][j] is key 32 kb + 8 (j / 4) + 4 lg + j % 4 of the tile, query myq.
+  auto qk = [&](const uint8_t* Ks, v16f (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       v16f acc;
@@ -291,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
           v8i kr = {0, 0, 0, 0, 0, 0, 0, 0};
           const uint4 x = *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]);
           kr[0] = x.x; kr[1] = x.y; kr[2] = x.z; kr[3] = x.w;
-          const int ksc = Ss[(32 * kb + lr) * (D / 32) + 2 * i + lg];
+          const int ksc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
           acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], acc, 4, 4, 0, ksc, 0,
                                                                 qsc[i]);
         }
@@ -305,28 +348,38 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       }
       s[kb] = acc;
     }
+  };
 
-    // ---- dequantisation factor c (log2 domain): c = sm_scale log2(e) / (s_Q s_K)
+  // Online softmax of the tile at key `ks` (scores s, V stage Vs) and
+  // O^T += V^T P~^T.  `overlap` runs just before the exponentials, in the same
+  // straight-line block, so that independent MFMAs can be interleaved with the
+  // softmax arithmetic.
+  auto softmax_pv = [&](const int ks, v16f (&s)[2], const uint8_t* Vs, auto overlap)
+      __attribute__((always_inline)) {
+    const uint8_t* Ms = Vs + TL::V_BYTES;
+    const float* Cs = reinterpret_cast<const float*>(Ms + TL::M_BYTES);
+    // dequantisation factor c (log2 domain): c = sm_scale log2(e) / (s_Q s_K),
     // per group of 4 keys (kb, j / 4); constant over the tile when UK.
     float c[8];
     if (MX) {
 #pragma unroll
       for (int g = 0; g < 8; ++g) c[g] = cq;
     } else if (UK) {
-      const float ck = cq * (1.0f / a.k_scale[(int64_t)bh * a.nblk_k + ks / a.blk_k]);
+      const float ck = cq * __builtin_amdgcn_rcpf(Cs[0]);
 #pragma unroll
       for (int g = 0; g < 8; ++g) c[g] = ck;
     } else {
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
-        c[g] = cq * (1.0f / a.k_scale[(int64_t)bh * a.nblk_k + (ks + 32 * (g / 4) + 8 * (g % 4)) / a.blk_k]);
+      for (int g = 0; g < 8; ++g) {   // Cs[i] is the scale of block ks / blk + i
+        const int key = ks + 32 * (g / 4) + 8 * (g % 4);
+        c[g] = cq * __builtin_amdgcn_rcpf(Cs[key / a.blk_k - ks / a.blk_k]);
+      }
     }
-
-    // ---- masks: padding keys (staged in LDS with the tile), keys past N,
-    // the causal diagonal; the test is wave-uniform
-    uint32_t kvw[8];
+    // masks: padding keys (staged in LDS with the tile), keys past N, the
+    // causal diagonal; the test is wave-uniform, the masking branch-free
+    uint32_t kvw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     bool partial = false;
-    if (a.kv_valid) {
+    if (hb.has_mask) {
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         kvw[g] = *reinterpret_cast<const uint32_t*>(Ms + 32 * (g / 4) + 8 * (g % 4) + 4 * lg);
@@ -336,33 +389,50 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const bool need_mask = (ks + kBN > a.N) || (MODE == 1 && ks + kBN - 1 > wq0) ||
                            (__builtin_amdgcn_ballot_w64(partial) != 0);
     if (need_mask) {
+      const int lim = MODE == 1 ? min(a.N - 1, myq) : a.N - 1;   // last admissible key
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = ks + 32 * kb + 8 * (j / 4) + 4 * lg + (j % 4);
-          bool ok = key < a.N;
-          if (a.kv_valid) ok = ok && (((kvw[4 * kb + j / 4] >> (8 * (j % 4))) & 0xFFu) != 0u);
-          if (MODE == 1) ok = ok && key <= myq;
-          if (!ok) s[kb][j] = kNegInf;
+          const uint32_t byte = (kvw[4 * kb + j / 4] >> (8 * (j % 4))) & 0xFFu;
+          const bool ok = (key <= lim) & (!hb.has_mask | (byte != 0u));
+          s[kb][j] = ok ? s[kb][j] : kNegInf;
         }
     }
-
-    // ---- online softmax: running max, P in the 448-scaled domain, E4M3
-    float mx = kNegInf;
+    // running max; with one factor c for the whole tile (c > 0) the max of
+    // c s is c times the max of s
+    float mx;
+    if (MX || UK) {
+      float m = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float m4 = fmaxf(fmaxf(s[kb][4 * g4], s[kb][4 * g4 + 1]),
-                               fmaxf(s[kb][4 * g4 + 2], s[kb][4 * g4 + 3]));
-        mx = fmaxf(mx, c[4 * kb + g4] * m4);
-      }
+        for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(s[kb][j], s[kb][j + 1]));
+      mx = c[0] * m;
+    } else {
+      mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float m4 = fmaxf(fmaxf(s[kb][4 * g4], s[kb][4 * g4 + 1]),
+                                 fmaxf(s[kb][4 * g4 + 2], s[kb][4 * g4 + 3]));
+          mx = fmaxf(mx, c[4 * kb + g4] * m4);
+        }
+    }
     mx = swap_max(mx);
     const float mnew = fmaxf(m_run, mx);
     const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
     const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448;
     m_run = mnew;
+    // conditional rescale of the running output
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha;
+    }
+    overlap();
+    // P in the 448-scaled domain, E4M3 in registers
     float sum = 0.0f;
     v8i pk;
 #pragma unroll
@@ -379,28 +449,64 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
         pk[4 * kb + g4] = w;
       }
-
-    // ---- conditional rescale of the running output
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    // interleave: the next tile's QK^T MFMAs (and their LDS operand reads)
+    // spread over the softmax arithmetic above
+    // (LDS reads run PRE_DS ahead of the MFMAs that consume them; the V
+    // operand reads of the P.V product join the same stream)
+    if (INTERLEAVE) {
+      __builtin_amdgcn_sched_group_barrier(0x100, PRE_DS, 0);    // LDS reads in flight
 #pragma unroll
-      for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha;
+      for (int i = 0; i < QK_MFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_MFMA, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0);
+      }
     }
     l_run = l_run * alpha + sum;
-
-    // ---- O^T += V^T P~^T (FP8 x FP8)
+    // O^T += V^T P~^T (FP8 x FP8)
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb) {
       const v8i vr = make_v8(*reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off0),
                              *reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off1));
       o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vr, pk, o[cb], 0, 0, 0, 127, 0, 127);
     }
-
-    wait_vm();
-    __syncthreads();
   };
-  for (int t = 0; t < n_steps; t += 2) {
-    step(t, stage0, stage1);
-    if (t + 1 < n_steps) step(t + 1, stage1, stage0);
+
+  // ---- prologue: K(0), V(0), K(1), V(1), K(2) in flight; wait for the first three.
+  // Past the last tile the copies repeat the last tile into stages nobody
+  // reads, which keeps the number of outstanding copies fixed.
+  auto tile_at = [&](int t) { return step_start(min(t, n_steps - 1)); };
+  issue_k<D, MX>(k0, hb, tile_at(0), wave, lane, kp);
+  issue_v<D, MX>(v0, hb, a.n_alloc, tile_at(0), wave, lane, vp);
+  issue_k<D, MX>(k1, hb, tile_at(1), wave, lane, kp);
+  issue_v<D, MX>(v1, hb, a.n_alloc, tile_at(1), wave, lane, vp);
+  issue_k<D, MX>(k2, hb, tile_at(2), wave, lane, kp);
+  wait_vm_le<NV + NK>();          // V(1) and K(2) may still be in flight
+  barrier_lds();
+
+  v16f s_cur[2], s_nxt[2];
+  qk(k0, s_cur);
+
+  // Iteration t with K stages (Kn1 = t+1, Kn3 = t+3) and V stages (Vc = t, Vn2 = t+2).
+  auto iter = [&](const int t, const uint8_t* Kn1, uint8_t* Kn3, const uint8_t* Vc, uint8_t* Vn2)
+      __attribute__((always_inline)) {
+    const int ks = step_start(t);
+    issue_k<D, MX>(Kn3, hb, tile_at(t + 3), wave, lane, kp);
+    issue_v<D, MX>(Vn2, hb, a.n_alloc, tile_at(t + 2), wave, lane, vp);
+    // (on the last iteration Kn1 holds a repeat of the last tile; the scores
+    // computed from it are not used - computing them keeps this code one
+    // straight-line block with the exponentials)
+    softmax_pv(ks, s_cur, Vc, [&]() __attribute__((always_inline)) { qk(Kn1, s_nxt); });
+    // K(t+2) and V(t+1) must have landed; this iteration's copies may not have
+    wait_vm_le<NK + NV>();
+    barrier_lds();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+  };
+  for (int t = 0; t < n_steps; t += 3) {
+    iter(t, k1, k0, v0, v2);
+    if (t + 1 < n_steps) iter(t + 1, k2, k1, v1, v0);
+    if (t + 2 < n_steps) iter(t + 2, k0, k2, v2, v1);
   }
 
   // ---- epilogue: O = acc / (448 l) / s_V, stored through the output permutation
