@@ -14,8 +14,16 @@ algorithmic FLOPs / time, with FLOPs = 4 N^2 d H for dense attention (causal:
 are computed).  `value` uses the whole step (quantisers + attention);
 `roofline` is for the attention kernel alone, timed with events on the stream
 it runs on.  `cpu_baseline` times the CPU oracle on a bounded sample.
+
+`roofline.traffic` (HBM bytes per attention launch) comes from the committed
+counter summary profiles/attention_<workload>_counters.md, made by two
+rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script with
+--copy-bytes, which adds a plain device copy of known size to calibrate the
+counters.  It is reported only while the attention kernel's sources hash to
+the value recorded there, and is null otherwise.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +41,51 @@ DEFAULT_CONFIG = "dense_mxfp4_16k"
 PEAK_FP8 = 5000.0
 PEAK_FP4 = 10100.0
 PEAK_BF16 = 2500.0
+# sources that define the attention kernel's code; a counter summary is valid
+# only for the sources it was taken on
+KERNEL_SOURCES = ("attention.hip", "pab_device.h", "pab_internal.h")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attention_%s_counters.md")
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "precision_attention_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None if there is none or the kernel sources changed since it was taken."""
+    path = TRAFFIC_SUMMARY % workload
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.split(":", 1)[0].strip() in (
+                    "kernel_sources_sha256", "traffic_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes, reps=3):
+    """A plain device-to-device copy of nbytes, for calibrating the HBM byte
+    counters (each launch reads and writes exactly nbytes)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def algorithmic_flops(cfg, plan=None):
@@ -186,6 +239,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, run a plain device copy of this many bytes "
+                         "(counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -238,8 +294,11 @@ def main():
                    "pct_fp8_peak": round(100 * achieved / PEAK_FP8, 2),
                    "pct_fp4_peak": round(100 * achieved / PEAK_FP4, 2) if cfg.recipe == "mxfp4" else None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(cfg.name)},
     }
+    if args.copy_bytes > 0:
+        copy_calibration(args.copy_bytes)
     if not args.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, x, path.plan and _oracle_plan(cfg), bn)
