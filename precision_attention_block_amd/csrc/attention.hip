@@ -33,10 +33,12 @@
 //  * the running output is rescaled only when some row maximum of the wave
 //    moved (conditional rescaling, FA4 co-design list; threshold 0, so the
 //    result equals an unconditional rescale).
-//  * K and V^T tiles are double-buffered in LDS and copied by LDS-DMA
-//    (buffer_load ... lds: no registers involved) into XOR-swizzled layouts
-//    with conflict-free 16-byte operand reads; the copy of the next tile is in
-//    flight while the current one is computed.
+//  * K and V^T tiles live in 3-stage LDS rings filled by LDS-DMA
+//    (buffer_load ... lds: no registers involved) in XOR-swizzled layouts
+//    with conflict-free 16-byte operand reads; copies run two to three tiles
+//    ahead of the tile being computed.
+//  * one wave keeps both units busy: the softmax of tile t is interleaved
+//    with the P.V MFMAs of tile t-1 and the QK^T MFMAs of tile t+1.
 //  * workgroups are dealt to XCDs so that all query tiles of a head share an
 //    L2; causal query tiles are issued longest-first (LPT).
 #include "pab_device.h"
@@ -47,6 +49,7 @@ namespace pab {
 constexpr float kNegInf = -__builtin_huge_valf();
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v8s __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Slot of 16-byte chunk c of row r in a swizzled LDS tile with CPR chunks per
@@ -65,17 +68,20 @@ struct Tile {
   static constexpr int KROW = MX ? D / 2 : 2 * D;   // bytes of one key row
   static constexpr int K_CPR = KROW / 16;
   static constexpr int K_BYTES = kBN * KROW;
-  static constexpr int S_BYTES = MX ? kBN * (D / 32) : 0;
+  static constexpr int S_BYTES = MX ? kBN * (D / 32) : 0;   // 256: one full-wave dword copy
   static constexpr int KBUF = K_BYTES + S_BYTES;
-  // V ring stage: V^T codes, the key padding mask and (FP8) the K block scales
-  static constexpr int V_BYTES = D * kBN;           // D rows of kBN E4M3 codes
-  static constexpr int M_BYTES = kBN;
-  static constexpr int C_BYTES = MX ? 0 : 16;       // K block scales of the tile (<= 4)
-  static constexpr int VBUF = V_BYTES + M_BYTES + C_BYTES;
+  // V ring stage: D rows of kBN E4M3 codes of V^T
+  static constexpr int VBUF = D * kBN;
+  // side ring stage: the key padding mask bytes and (FP8) the K block scales,
+  // each copied as one full-wave 256-byte LDS-DMA (only the first kBN mask
+  // bytes and the first few scales are used)
+  static constexpr int M_BYTES = 256;
+  static constexpr int ABUF = M_BYTES + (MX ? 0 : 256);
   static constexpr int KI = K_BYTES / 1024 / 4;     // LDS-DMA instructions per wave
-  static constexpr int VI = V_BYTES / 1024 / 4;
-  static_assert(KBUF % 16 == 0 && VBUF % 16 == 0, "LDS stages must stay 16-byte aligned");
-  static_assert(K_BYTES % 4096 == 0 && V_BYTES % 4096 == 0, "copy must split over 4 waves");
+  static constexpr int VI = VBUF / 1024 / 4;
+  static_assert(KBUF % 16 == 0 && VBUF % 16 == 0 && ABUF % 16 == 0,
+                "LDS stages must stay 16-byte aligned");
+  static_assert(K_BYTES % 4096 == 0 && VBUF % 4096 == 0, "copy must split over 4 waves");
 };
 
 // Lane offsets of the LDS-DMA copy of a region of rows (16 CPR bytes each,
@@ -106,13 +112,15 @@ struct HeadBuffers {
 };
 constexpr int kRsrcWord3 = 0x00020000;   // raw byte buffer
 
-// Every wave issues the same number of LDS-DMA instructions per stage (K for
-// a K stage, V for a V stage), and every pipeline iteration copies one K and
-// one V stage, so one outstanding-copy count serves every wave and iteration.
+// Every wave issues the same number of LDS-DMA instructions per copy (K for
+// a K stage, V for a V stage plus a side stage), and every pipeline iteration
+// issues one of each, so one outstanding-copy count serves every wave and
+// iteration.
 template <int D, bool MX>
 struct Issues {
   static constexpr int K = Tile<D, MX>::KI + (MX ? 1 : 0);
-  static constexpr int V = Tile<D, MX>::VI + 1 + (MX ? 0 : 1);
+  static constexpr int V = Tile<D, MX>::VI;
+  static constexpr int A = MX ? 1 : 2;
 };
 
 // Copies the K (and MXFP4 group scales) of the key tile at `ks` into a K stage.
@@ -127,18 +135,17 @@ __device__ inline void issue_k(uint8_t* kbuf, const HeadBuffers& hb, int ks, int
     __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16,
                                              kp.off[inst % KPER], (ks + inst * KRPI) * TL::KROW, 0, 0);
   }
-  if (MX && lane < 4)   // 256 bytes of E8M0 scales: 4 lanes x 16 bytes per wave
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(kbuf + TL::K_BYTES + 64 * wave), 16,
-                                             16 * (lane & 3), ks * (D / 32) + 64 * wave, 0, 0);
+  // the 256 bytes of E8M0 scales: one dword per lane; every wave copies the
+  // same bytes to the same place, which keeps the copy a full-wave one
+  if (MX)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(kbuf + TL::K_BYTES), 4, 4 * lane,
+                                             ks * (D / 32), 0, 0);
 }
 
-// Copies V^T, the padding mask and (FP8) the K block scales of the key tile at
-// `ks` into a V stage.  Each LDS-DMA instruction writes 16 bytes per active
-// lane, so the small copies run on lane 0 only (every wave copies the same K
-// scales to the same place, which is harmless).
+// Copies V^T of the key tile at `ks` into a V stage.
 template <int D, bool MX, typename VPlan>
 __device__ inline void issue_v(uint8_t* vbuf, const HeadBuffers& hb, int n_alloc, int ks, int wave,
-                               int lane, const VPlan& vp) {
+                               const VPlan& vp) {
   using TL = Tile<D, MX>;
 #pragma unroll
   for (int j = 0; j < TL::VI; ++j) {
@@ -146,12 +153,19 @@ __device__ inline void issue_v(uint8_t* vbuf, const HeadBuffers& hb, int n_alloc
     __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.v, (lds_void_t*)(vbuf + inst * 1024), 16, vp.off[0],
                                              ks + inst * 16 * n_alloc, 0, 0);
   }
-  if (lane == 0)   // 64 mask bytes, 16 per wave (zeros when there is no mask: ignored then)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.m, (lds_void_t*)(vbuf + TL::V_BYTES + 16 * wave), 16,
-                                             0, ks + 16 * wave, 0, 0);
-  if (!MX && lane == 0)   // the K block scales covering keys ks .. ks + BN - 1 (block size >= 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.c, (lds_void_t*)(vbuf + TL::V_BYTES + TL::M_BYTES),
-                                             16, 0, (ks / hb.blk_k) * 4, 0, 0);
+}
+
+// Copies the padding mask and (FP8) the K block scales of the key tile at `ks`
+// into a side stage: full-wave dword copies of 256 bytes each (past the end of
+// either buffer the copy reads zeros); every wave copies the same bytes to the
+// same place.
+template <int D, bool MX>
+__device__ inline void issue_aux(uint8_t* abuf, const HeadBuffers& hb, int ks, int lane) {
+  using TL = Tile<D, MX>;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.m, (lds_void_t*)abuf, 4, 4 * lane, ks, 0, 0);
+  if (!MX)   // scales of the blocks from ks / blk on (a tile spans at most 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.c, (lds_void_t*)(abuf + TL::M_BYTES), 4, 4 * lane,
+                                             (ks / hb.blk_k) * 4, 0, 0);
 }
 
 // Workgroup barrier that does not wait for outstanding LDS-DMA copies (a
@@ -178,11 +192,6 @@ __device__ inline v8i make_v8(uint4 lo, uint4 hi) {
   r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
   return r;
 }
-
-// True if some byte of w is zero.
-__device__ inline bool has_zero_byte(uint32_t w) {
-  return ((w - 0x01010101u) & ~w & 0x80808080u) != 0u;
-}
 #endif  // __HIP_DEVICE_COMPILE__
 
 __device__ inline float swap_max(float v) {
@@ -193,30 +202,35 @@ __device__ inline float swap_sum(float v) {
   auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
+__device__ inline float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // MODE: 0 dense, 1 causal (top-left aligned), 2 sliding-tile.
 // UK: the K scale is constant over each key tile (FP8 blocks a multiple of BN).
 //
-// Software pipeline over key tiles t = 0, 1, ...: iteration t issues the
-// copies of K(t+3) and V(t+2), the QK^T MFMAs of tile t+1, the softmax of
-// tile t (interleaved with those MFMAs) and the P.V MFMAs of tile t.  K and
-// V each have a 3-stage LDS ring, so every copy has two iterations to land.
+// Software pipeline over key tiles t = 0, 1, ...: iteration t
+//   - copies K(t+3) into a K stage, V(t+1) into a V stage and the mask/scales
+//     of tile t+2 into a side stage (3-stage rings; every copy has at least
+//     two iterations to land);
+//   - computes the online softmax of tile t from S(t), interleaved with the
+//     MFMAs of O^T += V(t-1)^T P~(t-1)^T and of S(t+1) = K(t+1) Q^T, so the
+//     matrix cores run while the vector ALUs exponentiate;
+//   - rescales O by alpha(t-1) first (the product of tile t-2 has landed).
+// Iteration t first rescales O by alpha(t-1) and then adds P~(t-1) V(t-1), so
+// after it O equals the eager accumulator after tile t-1
+// (acc(t-1) = alpha(t-1) acc(t-2) + P~(t-1) V(t-1)); the last tile's rescale
+// and product follow the loop.
 template <int D, bool MX, int MODE, bool UK>
-__global__ __launch_bounds__(256, (MX && MODE != 2) ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using TL = Tile<D, MX>;
   constexpr int DB = D / 32;            // 32-channel blocks of O^T
   constexpr int QI = D / 16;            // bf16 32x32x16 MFMAs over d (FP8 recipe)
-  constexpr int NK = Issues<D, MX>::K, NV = Issues<D, MX>::V;
-  constexpr int QK_MFMA = MX ? 4 : 2 * QI;          // QK^T MFMAs per key tile
-  constexpr int VALU_PER_MFMA = MX ? 30 : 8;
-  constexpr int PRE_DS = 8;                          // LDS reads issued ahead
-  constexpr int DS_PER_MFMA = MX ? 2 : 1;
-  constexpr bool INTERLEAVE = true;
+  constexpr int NK = Issues<D, MX>::K, NV = Issues<D, MX>::V, NA = Issues<D, MX>::A;
   // Distinct LDS objects per stage: the compiler can then see that a copy
   // into one stage does not alias reads of another and does not wait for it.
   __shared__ __align__(16) uint8_t k0[TL::KBUF], k1[TL::KBUF], k2[TL::KBUF];
   __shared__ __align__(16) uint8_t v0[TL::VBUF], v1[TL::VBUF], v2[TL::VBUF];
+  __shared__ __align__(16) uint8_t x0[TL::ABUF], x1[TL::ABUF], x2[TL::ABUF];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform; saying so keeps LDS-DMA addresses (M0) scalar
@@ -350,16 +364,99 @@ __global__ __launch_bounds__(256, (MX && MODE != 2) ? 3 : 2) void attn_fwd_kerne
     }
   };
 
-  // Online softmax of the tile at key `ks` (scores s, V stage Vs) and
-  // O^T += V^T P~^T.  `overlap` runs just before the exponentials, in the same
-  // straight-line block, so that independent MFMAs can be interleaved with the
-  // softmax arithmetic.
-  auto softmax_pv = [&](const int ks, v16f (&s)[2], const uint8_t* Vs, auto overlap)
+  // O^T += V^T P~^T (FP8 x FP8) for the tile in V stage `Vs`
+  auto pv = [&](const uint8_t* Vs, const v8i& pk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+      const v8i vr = make_v8(*reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off0),
+                             *reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off1));
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vr, pk, o[cb], 0, 0, 0, 127, 0, 127);
+    }
+  };
+
+  // The MFMAs of one pipeline iteration, in issue order: m < DB is the P.V
+  // product of channel block m; m >= DB is step m - DB of S = K Q^T (key
+  // block kb = (m - DB) / QPB, step i = (m - DB) % QPB).
+  constexpr int QPB = MX ? 2 : QI;
+  constexpr int NM = DB + 2 * QPB;
+  constexpr int LA = 2;                 // operand read lookahead, in slots
+  struct Op { v8i a; int sc; };
+  auto slot_lo = [](int g) constexpr { return g >= 8 ? NM : NM * g / 8; };
+  auto read_op = [&](const int m, const uint8_t* Vs, const uint8_t* Ks, Op& op)
       __attribute__((always_inline)) {
-    const uint8_t* Ms = Vs + TL::V_BYTES;
-    const float* Cs = reinterpret_cast<const float*>(Ms + TL::M_BYTES);
+    if (m < DB) {
+      op.a = make_v8(*reinterpret_cast<const uint4*>(Vs + m * 32 * kBN + v_off0),
+                     *reinterpret_cast<const uint4*>(Vs + m * 32 * kBN + v_off1));
+    } else {
+      const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
+      const uint4 x = *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]);
+      op.a[0] = x.x; op.a[1] = x.y; op.a[2] = x.z; op.a[3] = x.w;
+      if (MX) op.sc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
+    }
+  };
+  auto issue_op = [&](const int m, const Op& op, v16f (&acc)[2], const v8i& pk_in)
+      __attribute__((always_inline)) {
+    if (m < DB) {
+      o[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op.a, pk_in, o[m], 0, 0, 0, 127, 0, 127);
+    } else {
+      const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
+      v16f c0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c0[j] = 0.0f;
+      if (MX) {
+        v8i kr = {0, 0, 0, 0, 0, 0, 0, 0};
+        kr[0] = op.a[0]; kr[1] = op.a[1]; kr[2] = op.a[2]; kr[3] = op.a[3];
+        acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], i == 0 ? c0 : acc[kb],
+                                                                  4, 4, 0, op.sc, 0, qsc[i]);
+      } else {
+        v8s kr;
+        const v4i x = {op.a[0], op.a[1], op.a[2], op.a[3]};
+        kr = __builtin_bit_cast(v8s, x);
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qop16[i], i == 0 ? c0 : acc[kb], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- prologue.  V stage v2 stands for tile -1: zero codes, so the first
+  // iteration's product with the zero P adds nothing.
+  // Copies run up to three tiles past the last one.  Dense and causal tiles
+  // past the end read zeros or in-bounds bytes of the same head (buffer
+  // loads check their range) into stages that are never read; sliding-tile
+  // steps repeat the last tile, since the window list ends there.
+  auto tile_at = [&](int t) { return MODE == 2 ? step_start(min(t, n_steps - 1)) : t * kBN; };
+  issue_k<D, MX>(k0, hb, tile_at(0), wave, lane, kp);
+  issue_aux<D, MX>(x0, hb, tile_at(0), lane);
+  issue_k<D, MX>(k1, hb, tile_at(1), wave, lane, kp);
+  issue_aux<D, MX>(x1, hb, tile_at(1), lane);
+  issue_v<D, MX>(v0, hb, a.n_alloc, tile_at(0), wave, vp);
+  issue_k<D, MX>(k2, hb, tile_at(2), wave, lane, kp);
+#pragma unroll
+  for (int i = tid * 16; i < TL::VBUF; i += 256 * 16)
+    *reinterpret_cast<uint4*>(v2 + i) = make_uint4(0u, 0u, 0u, 0u);
+  wait_vm_le<NV + NK>();          // V(0) and K(2) may still be in flight
+  barrier_lds();
+
+  v16f sa[2], sb[2];
+  qk(k0, sa);
+  // P~ of the previous tile (read by the P.V MFMAs) and of the current one
+  // alternate between pa and pb like the score buffers
+  v8i pa = {0, 0, 0, 0, 0, 0, 0, 0}, pb;
+  barrier_lds();                  // every wave is done with k0 before K(3) is copied there
+  float alpha_prev = 1.0f;
+
+  // Iteration t: K stages Kr (t+1, read) and Kw (t+3, written); V stages Vr
+  // (t-1, read) and Vw (t+1, written); side stages Ar (t, read), Aw (t+2, written).
+  auto iter = [&](const int t, const uint8_t* Kr, uint8_t* Kw, const uint8_t* Vr, uint8_t* Vw,
+                  const uint8_t* Ar, uint8_t* Aw, v16f (&s_cur)[2], v16f (&s_nxt)[2],
+                  const v8i& pk_in, v8i& pk) __attribute__((always_inline)) {
+    const int ks = step_start(t);
+    issue_k<D, MX>(Kw, hb, tile_at(t + 3), wave, lane, kp);
+    issue_v<D, MX>(Vw, hb, a.n_alloc, tile_at(t + 1), wave, vp);
+    issue_aux<D, MX>(Aw, hb, tile_at(t + 2), lane);
+
     // dequantisation factor c (log2 domain): c = sm_scale log2(e) / (s_Q s_K),
     // per group of 4 keys (kb, j / 4); constant over the tile when UK.
+    const float* Cs = reinterpret_cast<const float*>(Ar + TL::M_BYTES);
     float c[8];
     if (MX) {
 #pragma unroll
@@ -375,40 +472,56 @@ __global__ __launch_bounds__(256, (MX && MODE != 2) ? 3 : 2) void attn_fwd_kerne
         c[g] = cq * __builtin_amdgcn_rcpf(Cs[key / a.blk_k - ks / a.blk_k]);
       }
     }
-    // masks: padding keys (staged in LDS with the tile), keys past N, the
-    // causal diagonal; the test is wave-uniform, the masking branch-free
-    uint32_t kvw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    bool partial = false;
-    if (hb.has_mask) {
+    // O = alpha(t-1) O: the product of tile t-2 (issued one iteration ago)
+    // has landed, that of tile t-1 is issued below; only when some row max
+    // moved
+    if (__builtin_amdgcn_ballot_w64(alpha_prev != 1.0f) != 0) {
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        kvw[g] = *reinterpret_cast<const uint32_t*>(Ms + 32 * (g / 4) + 8 * (g % 4) + 4 * lg);
-        partial |= has_zero_byte(kvw[g]);
+      for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha_prev;
+    }
+    // masks: padding keys (staged with the tile), keys past N, the causal
+    // diagonal; the tests are wave-uniform, the masking branch-free
+    const bool edge = (ks + kBN > a.N) || (MODE == 1 && ks + kBN - 1 > wq0);
+    if (edge || hb.has_mask) {
+      const bool partial = hb.has_mask && Ar[lane] == 0;
+      if (edge || __builtin_amdgcn_ballot_w64(partial) != 0) {
+        const int lim = MODE == 1 ? min(a.N - 1, myq) : a.N - 1;   // last admissible key
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const uint32_t w = hb.has_mask
+                ? *reinterpret_cast<const uint32_t*>(Ar + 32 * kb + 8 * g4 + 4 * lg) : 0x01010101u;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int key = ks + 32 * kb + 8 * g4 + 4 * lg + jj;
+              const bool ok = (key <= lim) & (((w >> (8 * jj)) & 0xFFu) != 0u);
+              s_cur[kb][4 * g4 + jj] = ok ? s_cur[kb][4 * g4 + jj] : kNegInf;
+            }
+          }
       }
     }
-    const bool need_mask = (ks + kBN > a.N) || (MODE == 1 && ks + kBN - 1 > wq0) ||
-                           (__builtin_amdgcn_ballot_w64(partial) != 0);
-    if (need_mask) {
-      const int lim = MODE == 1 ? min(a.N - 1, myq) : a.N - 1;   // last admissible key
+
+    // operands of the first LA slots
+    Op ops[NM];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = ks + 32 * kb + 8 * (j / 4) + 4 * lg + (j % 4);
-          const uint32_t byte = (kvw[4 * kb + j / 4] >> (8 * (j % 4))) & 0xFFu;
-          const bool ok = (key <= lim) & (!hb.has_mask | (byte != 0u));
-          s[kb][j] = ok ? s[kb][j] : kNegInf;
-        }
-    }
+    for (int m = 0; m < slot_lo(LA); ++m) read_op(m, Vr, Kr, ops[m]);
+
     // running max; with one factor c for the whole tile (c > 0) the max of
     // c s is c times the max of s
     float mx;
     if (MX || UK) {
-      float m = kNegInf;
+      // max3 tree over the lane's 32 scores
+      float m11[11];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(s[kb][j], s[kb][j + 1]));
+      for (int i = 0; i < 10; ++i) {
+        const int e = 3 * i;
+        m11[i] = max3f(s_cur[e / 16][e % 16], s_cur[(e + 1) / 16][(e + 1) % 16],
+                       s_cur[(e + 2) / 16][(e + 2) % 16]);
+      }
+      m11[10] = fmaxf(s_cur[1][14], s_cur[1][15]);
+      const float m = max3f(max3f(m11[0], m11[1], m11[2]), max3f(m11[3], m11[4], m11[5]),
+                            max3f(max3f(m11[6], m11[7], m11[8]), m11[9], m11[10]));
       mx = c[0] * m;
     } else {
       mx = kNegInf;
@@ -416,8 +529,8 @@ __global__ __launch_bounds__(256, (MX && MODE != 2) ? 3 : 2) void attn_fwd_kerne
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const float m4 = fmaxf(fmaxf(s[kb][4 * g4], s[kb][4 * g4 + 1]),
-                                 fmaxf(s[kb][4 * g4 + 2], s[kb][4 * g4 + 3]));
+          const float m4 = fmaxf(fmaxf(s_cur[kb][4 * g4], s_cur[kb][4 * g4 + 1]),
+                                 fmaxf(s_cur[kb][4 * g4 + 2], s_cur[kb][4 * g4 + 3]));
           mx = fmaxf(mx, c[4 * kb + g4] * m4);
         }
     }
@@ -426,88 +539,71 @@ __global__ __launch_bounds__(256, (MX && MODE != 2) ? 3 : 2) void attn_fwd_kerne
     const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
     const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448;
     m_run = mnew;
-    // conditional rescale of the running output
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+
+    // The previous tile's P.V and the next tile's S are independent MFMAs;
+    // they are dealt over 8 slots, one per group of 4 exponentials, and each
+    // slot's operands are read from LDS LA slots ahead (a slot is shorter
+    // than an LDS read's latency).  The order is pinned
+    // with empty volatile asm statements (kept in program order): a slot's
+    // MFMAs take their operands from one, and its exponentials end in one.
+    float gs[8];
+    v16f acc[2];
 #pragma unroll
-      for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha;
-    }
-    overlap();
-    // P in the 448-scaled domain, E4M3 in registers
-    float sum = 0.0f;
-    v8i pk;
+    for (int g = 0; g < 8; ++g) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float cc = c[4 * kb + g4];
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * g4 + 0], cc, -msh));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * g4 + 1], cc, -msh));
-        const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * g4 + 2], cc, -msh));
-        const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * g4 + 3], cc, -msh));
-        sum += (p0 + p1) + (p2 + p3);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
-        pk[4 * kb + g4] = w;
+      for (int m = slot_lo(g); m < slot_lo(g + 1); ++m) {
+        asm volatile("" : "+v"(ops[m].a));
+        issue_op(m, ops[m], acc, pk_in);
       }
-    // interleave: the next tile's QK^T MFMAs (and their LDS operand reads)
-    // spread over the softmax arithmetic above
-    // (LDS reads run PRE_DS ahead of the MFMAs that consume them; the V
-    // operand reads of the P.V product join the same stream)
-    if (INTERLEAVE) {
-      __builtin_amdgcn_sched_group_barrier(0x100, PRE_DS, 0);    // LDS reads in flight
 #pragma unroll
-      for (int i = 0; i < QK_MFMA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_MFMA, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0);
-      }
+      for (int m = slot_lo(g + LA); m < slot_lo(g + LA + 1); ++m) read_op(m, Vr, Kr, ops[m]);
+      const int kb = g / 4, g4 = g % 4;
+      const float cc = c[g];
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + 0], cc, -msh));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + 1], cc, -msh));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + 2], cc, -msh));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + 3], cc, -msh));
+      gs[g] = (p0 + p1) + (p2 + p3);
+      int w;
+      asm volatile("" : "=v"(w));   // the two conversions below write all four bytes
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, w, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+      asm volatile("" : "+v"(w), "+v"(gs[g]));
+      pk[g] = w;
     }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_nxt[kb] = acc[kb];
+    const float sum = ((gs[0] + gs[1]) + (gs[2] + gs[3])) + ((gs[4] + gs[5]) + (gs[6] + gs[7]));
     l_run = l_run * alpha + sum;
-    // O^T += V^T P~^T (FP8 x FP8)
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb) {
-      const v8i vr = make_v8(*reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off0),
-                             *reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off1));
-      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vr, pk, o[cb], 0, 0, 0, 127, 0, 127);
-    }
-  };
-
-  // ---- prologue: K(0), V(0), K(1), V(1), K(2) in flight; wait for the first three.
-  // Past the last tile the copies repeat the last tile into stages nobody
-  // reads, which keeps the number of outstanding copies fixed.
-  auto tile_at = [&](int t) { return step_start(min(t, n_steps - 1)); };
-  issue_k<D, MX>(k0, hb, tile_at(0), wave, lane, kp);
-  issue_v<D, MX>(v0, hb, a.n_alloc, tile_at(0), wave, lane, vp);
-  issue_k<D, MX>(k1, hb, tile_at(1), wave, lane, kp);
-  issue_v<D, MX>(v1, hb, a.n_alloc, tile_at(1), wave, lane, vp);
-  issue_k<D, MX>(k2, hb, tile_at(2), wave, lane, kp);
-  wait_vm_le<NV + NK>();          // V(1) and K(2) may still be in flight
-  barrier_lds();
-
-  v16f s_cur[2], s_nxt[2];
-  qk(k0, s_cur);
-
-  // Iteration t with K stages (Kn1 = t+1, Kn3 = t+3) and V stages (Vc = t, Vn2 = t+2).
-  auto iter = [&](const int t, const uint8_t* Kn1, uint8_t* Kn3, const uint8_t* Vc, uint8_t* Vn2)
-      __attribute__((always_inline)) {
-    const int ks = step_start(t);
-    issue_k<D, MX>(Kn3, hb, tile_at(t + 3), wave, lane, kp);
-    issue_v<D, MX>(Vn2, hb, a.n_alloc, tile_at(t + 2), wave, lane, vp);
-    // (on the last iteration Kn1 holds a repeat of the last tile; the scores
-    // computed from it are not used - computing them keeps this code one
-    // straight-line block with the exponentials)
-    softmax_pv(ks, s_cur, Vc, [&]() __attribute__((always_inline)) { qk(Kn1, s_nxt); });
-    // K(t+2) and V(t+1) must have landed; this iteration's copies may not have
-    wait_vm_le<NK + NV>();
+    alpha_prev = alpha;
+    // K(t+2), V(t) and the side stage of t+1 must have landed; this
+    // iteration's copies may not have
+    wait_vm_le<NK + NV + NA>();
     barrier_lds();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
   };
-  for (int t = 0; t < n_steps; t += 3) {
-    iter(t, k1, k0, v0, v2);
-    if (t + 1 < n_steps) iter(t + 1, k2, k1, v1, v0);
-    if (t + 2 < n_steps) iter(t + 2, k0, k2, v2, v1);
+  // unrolled by 6: the stage rings have period 3 and the two score buffers
+  // alternate, so no buffer is ever copied
+  for (int t = 0; t < n_steps; t += 6) {
+    iter(t, k1, k0, v2, v1, x0, x2, sa, sb, pa, pb);
+    if (t + 1 < n_steps) iter(t + 1, k2, k1, v0, v2, x1, x0, sb, sa, pb, pa);
+    if (t + 2 < n_steps) iter(t + 2, k0, k2, v1, v0, x2, x1, sa, sb, pa, pb);
+    if (t + 3 < n_steps) iter(t + 3, k1, k0, v2, v1, x0, x2, sb, sa, pb, pa);
+    if (t + 4 < n_steps) iter(t + 4, k2, k1, v0, v2, x1, x0, sa, sb, pa, pb);
+    if (t + 5 < n_steps) iter(t + 5, k0, k2, v1, v0, x2, x1, sb, sa, pb, pa);
   }
+  // the last tile's product: V(n_steps - 1) sits in stage (n_steps - 1) % 3
+  {
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha_prev;
+    const int r = (n_steps - 1) % 3;
+    pv(r == 0 ? v0 : r == 1 ? v1 : v2, (n_steps & 1) ? pb : pa);
+    // keep these MFMAs here, with every lane active: sunk into the store
+    // branch below they would run on a partial EXEC mask, which drops the
+    // operand rows of the inactive lanes
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) asm volatile("" : "+v"(o[cb]));
+  }
+  wait_vm_le<0>();   // no copy may still target this workgroup's LDS when it ends
 
   // ---- epilogue: O = acc / (448 l) / s_V, stored through the output permutation
   const float lt = swap_sum(l_run);
