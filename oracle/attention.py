@@ -89,7 +89,6 @@ def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None
     m = np.full(r, -np.inf, dtype=ftype)
     l = np.zeros(r)
     acc = np.zeros((r, d))
-    vdec = e4m3_decode(v.codes)
     if key_blocks is None:
         key_blocks = range(0, n, bn)
     for t0 in key_blocks:
@@ -116,7 +115,7 @@ def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None
             pq = e4m3_decode(e4m3_encode(np.float32(448.0) * p.astype(np.float32)))
         else:
             pq = 448.0 * p.astype(np.float64)
-        acc = alpha[:, None] * acc + pq @ vdec[cols]
+        acc = alpha[:, None] * acc + pq @ e4m3_decode(v.codes[cols])
         m = m_new
     with np.errstate(invalid="ignore", divide="ignore"):
         o = acc / l[:, None] / 448.0 / v.scales.astype(np.float64)[None, :]

@@ -1,0 +1,87 @@
+"""Oracle side of the full-size parity tests.
+
+The oracle is run per head in spawned worker processes (CPU only: this module
+imports neither torch nor the GPU library).  Workers read the float32 inputs
+[1, H, N_real, d] from shared memory created by the test, quantise their
+head with the oracle quantizers (after the 3D token reorder for grid
+workloads), run the oracle recipe for that head's sampled query rows and
+return the rows plus digests of the codes and scales, which the test compares
+with digests of the GPU's codes.
+"""
+import hashlib
+from multiprocessing import shared_memory
+
+import numpy as np
+
+from oracle import attention as OA
+from oracle import quant as OQ
+from oracle import sta as OS
+from workloads import CONFIGS
+
+FULL_WINDOW = (99, 99, 99)     # window reaching every tile (dense on a grid)
+
+
+def digest(*arrays):
+    h = hashlib.sha256()
+    for a in arrays:
+        a = np.ascontiguousarray(a)
+        h.update(str(a.dtype).encode())
+        h.update(str(a.shape).encode())
+        h.update(a.tobytes())
+    return h.hexdigest()
+
+
+def oracle_plan(cfg):
+    return OS.plan(cfg.grid, cfg.real_grid, cfg.tile, cfg.window if cfg.window else FULL_WINDOW)
+
+
+def kernel_positions(plan, tokens):
+    """Kernel (tile-major) positions of raster tokens."""
+    ok = plan.perm >= 0
+    inv = np.empty(int(ok.sum()), np.int64)
+    inv[plan.perm[ok]] = np.nonzero(ok)[0]
+    return inv[tokens]
+
+
+def head_job(job):
+    """(config name, shm names, shape, head, raster tokens, bn) ->
+    (head, tokens, oracle rows [len, d] float32, digests)."""
+    name, shm_names, shape, head, tokens, bn = job
+    cfg = CONFIGS[name]
+    blocks = [shared_memory.SharedMemory(name=n) for n in shm_names]
+    try:
+        q, k, v = (np.ndarray(shape, np.float32, buffer=b.buf)[0, head].copy() for b in blocks)
+    finally:
+        for b in blocks:
+            b.close()
+    kv_valid, plan = None, None
+    rows = np.asarray(tokens, np.int64)
+    if cfg.grid is not None:
+        plan = oracle_plan(cfg)
+        q, k, v = (OS.gather_tokens(a[None], plan.perm)[0] for a in (q, k, v))
+        kv_valid = plan.kv_valid
+        rows = kernel_positions(plan, rows)
+    if cfg.recipe == "fp8":
+        qc, qs = OQ.fp8_block_quantize(q, cfg.blk)
+        kc, ks = OQ.fp8_block_quantize(k, cfg.blk)
+        qo, ko = OA.Operand("fp8_block", qc, qs, cfg.blk), OA.Operand("fp8_block", kc, ks, cfg.blk)
+    else:
+        qc, qs = OQ.mxfp4_quantize(q)
+        kc, ks = OQ.mxfp4_quantize(k)
+        qo, ko = OA.Operand("mxfp4", qc, qs), OA.Operand("mxfp4", kc, ks)
+    vc, vs = OQ.fp8_channel_quantize(v)
+    vo = OA.Operand("fp8_channel", vc, vs)
+    digests = {"q": digest(qc, qs), "k": digest(kc, ks), "v": digest(vc, vs)}
+    sm = 1.0 / np.sqrt(cfg.d)
+    out = np.zeros((len(rows), cfg.d), np.float32)
+    if cfg.mode == "sta":
+        tiles = rows // plan.tile_tokens
+        for u in np.unique(tiles):
+            sel = np.nonzero(tiles == u)[0]
+            kb = OS.key_blocks_for_tile(plan, int(u), bn)
+            out[sel] = OA.recipe_attention(qo, ko, vo, rows[sel], sm_scale=sm, bn=bn,
+                                           kv_valid=kv_valid, key_blocks=kb)
+    else:
+        out[:] = OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm, bn=bn,
+                                     causal=cfg.mode == "causal", kv_valid=kv_valid)
+    return head, tokens, out, digests

@@ -1,0 +1,115 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times: 4096 seeded (head, query) rows per workload (drawn uniformly over heads
+x real tokens) are checked against the oracle, and every sampled head's codes
+and scales must equal the oracle's bit for bit.  The oracle runs per head in
+spawned CPU worker processes (tests/fullsize.py) while the GPU computes."""
+import multiprocessing as mp
+import os
+from multiprocessing import shared_memory
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as OF
+from tests import fullsize as FS
+from tests.helpers import MAX_ABS, MEAN_ABS, vt_to_tokens
+from workloads import CONFIGS, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+ROWS = int(os.environ.get("PAB_FULLSIZE_ROWS", "4096"))
+WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _gpu_run(lib, cfg, x):
+    """quantise + attention exactly as bench.py's step does; returns the
+    quantised tensors and the output."""
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev) for n in ("q_t", "k_t", "v_t"))
+    plan = dplan = None
+    if cfg.grid is not None:
+        plan = lib.sta_plan(cfg.grid, cfg.real_grid, cfg.tile, cfg.window or FS.FULL_WINDOW)
+        dplan = lib.DevicePlan(plan, dev)
+    perm = dplan.perm if dplan is not None else None
+    n_out = cfg.n_kernel
+    if cfg.recipe == "fp8":
+        qq = lib.quantize(q, "fp8_block", cfg.blk, perm, n_out)
+        kq = lib.quantize(k, "fp8_block", cfg.blk, perm, n_out)
+    else:
+        qq = lib.quantize(q, "mxfp4", None, perm, n_out)
+        kq = lib.quantize(k, "mxfp4", None, perm, n_out)
+    vq = lib.quantize(v, "fp8_channel", None, perm, n_out)
+    del q, k, v
+    if cfg.mode == "sta":
+        out = lib.attention_sta(qq, kq, vq, dplan)
+    elif dplan is not None:
+        out = lib.attention_dense(qq, kq, vq, kv_valid=dplan.kv_valid, out_perm=dplan.perm,
+                                  n_out=cfg.n_real)
+    else:
+        out = lib.attention_dense(qq, kq, vq, causal=cfg.mode == "causal")
+    torch.cuda.synchronize()
+    return qq, kq, vq, out
+
+
+def _gpu_digests(cfg, qq, kq, vq, head):
+    n = cfg.n_kernel
+    out = {}
+    for name, t in (("q", qq), ("k", kq)):
+        codes = t.codes[0, head].cpu().numpy()[:n]
+        if cfg.recipe == "fp8":
+            nb = -(-n // cfg.blk)
+            out[name] = FS.digest(codes, t.scales[0, head].cpu().numpy()[:nb])
+        else:
+            out[name] = FS.digest(OF.e2m1_unpack(codes), t.scales[0, head].cpu().numpy()[:n])
+    vt = vq.codes[0, head].cpu().numpy()
+    out["v"] = FS.digest(vt_to_tokens(vt, n), vq.scales[0, head].cpu().numpy())
+    return out
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llm_prefill_fp8_causal", "dense_mxfp4_16k", "dense_fp8_16k",
+                                  "sta_46k_fp8", "video_92k_fp8_dense", "video_92k_fp8_sta"])
+def test_full_size_sampled_rows(gpu_lib, name):
+    cfg = CONFIGS[name]
+    print("full size", name, "rows", ROWS, "workers", WORKERS, flush=True)
+    x = make_inputs(cfg, as_torch=True)
+    mode = {"dense": 0, "causal": 1, "sta": 2}[cfg.mode]
+    _, bn = gpu_lib.attention_info("mxfp4" if cfg.recipe == "mxfp4" else "fp8_block", cfg.d, mode)
+    heads, tokens = sample_rows(cfg, ROWS)
+    shms = []
+    try:
+        for n in ("q", "k", "v"):
+            a = x[n]
+            shm = shared_memory.SharedMemory(create=True, size=a.nbytes)
+            shms.append(shm)
+            np.ndarray(a.shape, np.float32, buffer=shm.buf)[:] = a
+        shape = x["q"].shape
+        jobs = [(name, [s.name for s in shms], shape, int(h), tokens[heads == h], bn)
+                for h in np.unique(heads)]
+        with mp.get_context("spawn").Pool(WORKERS) as pool:
+            pending = pool.imap_unordered(FS.head_job, jobs, chunksize=1)
+            qq, kq, vq, out = _gpu_run(gpu_lib, cfg, x)
+            print("  gpu done", flush=True)
+            results = []
+            for r in pending:
+                results.append(r)
+                if len(results) % 8 == 0 or len(results) == len(jobs):
+                    print("  oracle heads %d/%d" % (len(results), len(jobs)), flush=True)
+    finally:
+        for s in shms:
+            s.close()
+            s.unlink()
+    print("  oracle done", flush=True)
+    worst, total, count = 0.0, 0.0, 0
+    for head, toks, ref, dig in results:
+        assert _gpu_digests(cfg, qq, kq, vq, head) == dig, "codes or scales differ, head %d" % head
+        got = out[0, head, torch.from_numpy(toks).to(out.device)].cpu().numpy()
+        assert np.all(np.isfinite(got)), "non-finite output, head %d" % head
+        err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+        worst = max(worst, float(err.max()))
+        total += float(err.sum())
+        count += err.size
+    mean = total / count
+    print("  %s: %d rows, max-abs %.3g mean-abs %.3g" % (name, len(heads), worst, mean), flush=True)
+    assert worst <= MAX_ABS and mean <= MEAN_ABS, (worst, mean)
