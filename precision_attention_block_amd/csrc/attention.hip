@@ -379,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // block kb = (m - DB) / QPB, step i = (m - DB) % QPB).
   constexpr int QPB = MX ? 2 : QI;
   constexpr int NM = DB + 2 * QPB;
-  constexpr int LA = 2;                 // operand read lookahead, in slots
+  constexpr int LA = MX ? 2 : 1;        // operand read lookahead, in slots
   struct Op { v8i a; int sc; };
   auto slot_lo = [](int g) constexpr { return g >= 8 ? NM : NM * g / 8; };
   auto read_op = [&](const int m, const uint8_t* Vs, const uint8_t* Ks, Op& op)
@@ -548,6 +548,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // MFMAs take their operands from one, and its exponentials end in one.
     float gs[8];
     v16f acc[2];
+    float pq[4];   // exponentials of the previous group, packed one slot later
+    // packs group g's four P values to E4M3 and sums them; runs one slot after
+    // their exponentials so that the exp latency is hidden by other work
+    auto finish = [&](const int g) __attribute__((always_inline)) {
+      gs[g] = (pq[0] + pq[1]) + (pq[2] + pq[3]);
+      int w;
+      asm volatile("" : "=v"(w));   // the two conversions below write all four bytes
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], w, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], w, true);
+      asm volatile("" : "+v"(w), "+v"(gs[g]));
+      pk[g] = w;
+    };
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
 #pragma unroll
@@ -559,18 +571,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       for (int m = slot_lo(g + LA); m < slot_lo(g + LA + 1); ++m) read_op(m, Vr, Kr, ops[m]);
       const int kb = g / 4, g4 = g % 4;
       const float cc = c[g];
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + 0], cc, -msh));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + 1], cc, -msh));
-      const float p2 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + 2], cc, -msh));
-      const float p3 = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + 3], cc, -msh));
-      gs[g] = (p0 + p1) + (p2 + p3);
-      int w;
-      asm volatile("" : "=v"(w));   // the two conversions below write all four bytes
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, w, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
-      asm volatile("" : "+v"(w), "+v"(gs[g]));
-      pk[g] = w;
+      float pn[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pn[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + j], cc, -msh));
+      if (g > 0) finish(g - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pq[j] = pn[j];
     }
+    finish(7);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_nxt[kb] = acc[kb];
     const float sum = ((gs[0] + gs[1]) + (gs[2] + gs[3])) + ((gs[4] + gs[5]) + (gs[6] + gs[7]));
