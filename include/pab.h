@@ -81,7 +81,8 @@ int pab_last_hip_error(void);
 int64_t pab_token_alloc(int64_t n);
 
 /* Tile sizes of the attention kernel for a recipe / head dim: BM queries per
- * workgroup (128), BN keys per online-softmax step (64).  The online softmax visits key
+ * workgroup (256 for dense FP8 attention with d = 128, else 128), BN keys per
+ * online-softmax step (64).  The online softmax visits key
  * tiles of BN keys in ascending order and requantises P against the running
  * maximum including the current tile, so BN is part of the result's
  * definition (the reference oracle takes it as a parameter).

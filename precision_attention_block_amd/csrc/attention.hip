@@ -640,6 +640,434 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant for dense and causal attention with d = 128.
+//
+// A workgroup of 8 waves owns 256 queries of one head (32 per wave).  Waves w
+// and w + 4 share a SIMD; they form two groups that alternate between a
+// vector phase (the online softmax of tile t: masks, max, exponentials, P~
+// packing, row sums, rescale of O) and a matrix phase (O^T += V(t)^T P~(t)^T
+// and S(t+1) = K(t+1) Q^T), switching at every workgroup barrier, so that one
+// wave's MFMAs run while the other wave's exponentials use the vector ALU.
+// Per tile t the order of operations of each wave is the eager one:
+// softmax(t) rescales O by alpha(t), then P~(t) V(t) is added.
+//
+//   step 2t    group 0: vector phase t       group 1: matrix phase t-1
+//   step 2t+1  group 0: matrix phase t       group 1: vector phase t
+//
+// Tiles live in 4-stage LDS rings (K, V^T, side data).  At the start of its
+// matrix phase t each wave copies its share of K(t+3), V(t+2) and the side
+// data of t+2 (group 1 one step after group 0), and at the end of it waits
+// for its copies of the previous iteration.  Every wave issues the same
+// number of LDS-DMA instructions per iteration.
+template <bool MX>
+struct PP {
+  static constexpr int D = 128;
+  using TL = Tile<D, MX>;
+  static constexpr int NST = 4;                         // ring stages
+  static constexpr int BMW = 256;                       // queries per workgroup
+  // K copy: FP8 16 x 1 KB instructions (2 per wave); MXFP4 4 x 1 KB (waves
+  // 0-3) plus the 256 E8M0 scale bytes (waves 4-7)
+  static constexpr int KI8 = MX ? 1 : TL::K_BYTES / 1024 / 8;
+  static constexpr int VI8 = TL::VBUF / 1024 / 8;        // 1
+  static constexpr int NA = MX ? 1 : 2;
+  static constexpr int ISSUES = KI8 + VI8 + NA;
+  static_assert(VI8 == 1 && (MX || KI8 == 2), "copy split assumes d = 128");
+};
+
+#if defined(__HIP_DEVICE_COMPILE__)
+template <bool MX, typename KPlan>
+__device__ inline void pp_issue_k(uint8_t* kbuf, const HeadBuffers& hb, int ks, int wave, int lane,
+                                  const KPlan& kp) {
+  using TL = typename PP<MX>::TL;
+  constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI, KPER = DmaPlan<TL::K_CPR>::PER;
+  if (MX) {
+    if (wave < 4) {
+      const int inst = wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16,
+                                               kp.off[inst % KPER], (ks + inst * KRPI) * TL::KROW, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(kbuf + TL::K_BYTES), 4, 4 * lane,
+                                               ks * (PP<MX>::D / 32), 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PP<MX>::KI8; ++j) {
+      const int inst = wave + 8 * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16,
+                                               kp.off[inst % KPER], (ks + inst * KRPI) * TL::KROW, 0, 0);
+    }
+  }
+}
+
+template <bool MX, typename VPlan>
+__device__ inline void pp_issue_v(uint8_t* vbuf, const HeadBuffers& hb, int n_alloc, int ks, int wave,
+                                  const VPlan& vp) {
+  const int inst = wave;   // 8 x 1 KB: 16 channel rows of kBN codes each
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.v, (lds_void_t*)(vbuf + inst * 1024), 16, vp.off[0],
+                                           ks + inst * 16 * n_alloc, 0, 0);
+}
+#endif  // __HIP_DEVICE_COMPILE__
+
+template <bool MX, int MODE, bool UK>
+__global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using P = PP<MX>;
+  using TL = typename P::TL;
+  constexpr int D = P::D;
+  constexpr int DB = D / 32;
+  constexpr int QI = D / 16;
+  __shared__ __align__(16) uint8_t k0[TL::KBUF], k1[TL::KBUF], k2[TL::KBUF], k3[TL::KBUF];
+  __shared__ __align__(16) uint8_t v0[TL::VBUF], v1[TL::VBUF], v2[TL::VBUF], v3[TL::VBUF];
+  __shared__ __align__(16) uint8_t x0[TL::ABUF], x1[TL::ABUF], x2[TL::ABUF], x3[TL::ABUF];
+  uint8_t* const KS[4] = {k0, k1, k2, k3};
+  uint8_t* const VS[4] = {v0, v1, v2, v3};
+  uint8_t* const XS[4] = {x0, x1, x2, x3};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int work = xcd_work_index(blockIdx.x, gridDim.x);
+  const int n_qt = (a.n_alloc + P::BMW - 1) / P::BMW;
+  const int bh = work / n_qt;
+  int qt = work % n_qt;
+  if (MODE == 1) qt = n_qt - 1 - qt;   // longest query tiles first
+  const int q0 = qt * P::BMW;
+  const int all = (a.N + kBN - 1) / kBN;
+  const int n_steps = MODE == 1 ? min((q0 + P::BMW) / kBN, all) : all;
+  const int wq0 = q0 + wave * 32;
+  const int myq = wq0 + lr;
+  const bool q_live = wq0 < a.n_alloc;      // the wave's 32 queries have token slots
+
+  const int64_t tok0 = (int64_t)bh * a.n_alloc;
+  const uint8_t* kbh = (MX ? a.k : a.k16) + tok0 * TL::KROW;
+  const uint8_t* vbh = a.vt + (int64_t)bh * D * a.n_alloc;
+
+  v8s qop16[QI];
+  v8i qop8[2];
+  int qsc[2] = {127, 127};
+  float cq = a.sm_log2;
+  {
+    const int64_t qrow = tok0 + (q_live ? myq : 0);
+    if (MX) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (q_live) {
+          const uint4 x = *reinterpret_cast<const uint4*>(a.q + qrow * (D / 2) + 16 * (2 * i + lg));
+          r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+          qsc[i] = a.q_mx[qrow * (D / 32) + 2 * i + lg];
+        }
+        qop8[i] = r;
+      }
+    } else {
+      const uint8_t* qp = a.q16 + qrow * (2 * D) + 16 * QI * lg;
+#pragma unroll
+      for (int i = 0; i < QI; ++i) {
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (q_live) x = *reinterpret_cast<const uint4*>(qp + 16 * i);
+        qop16[i] = __builtin_bit_cast(v8s, x);
+      }
+      if (q_live) cq = a.sm_log2 / a.q_scale[(int64_t)bh * a.nblk_q + myq / a.blk_q];
+    }
+  }
+
+  float m_run = kNegInf, l_run = 0.0f;
+  v16f o[DB];
+#pragma unroll
+  for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[cb][j] = 0.0f;
+
+  DmaPlan<TL::K_CPR> kp;
+  DmaPlan<4> vp;
+  kp.init(lane, TL::KROW);
+  vp.init(lane, a.n_alloc);
+  HeadBuffers hb;
+  hb.k = __builtin_amdgcn_make_buffer_rsrc((void*)kbh, 0, a.n_alloc * TL::KROW, kRsrcWord3);
+  hb.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbh, 0, a.n_alloc * D, kRsrcWord3);
+  hb.s = __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? a.k_mx + tok0 * (D / 32) : kbh), 0,
+                                           MX ? a.n_alloc * (D / 32) : 0, kRsrcWord3);
+  hb.has_mask = a.kv_valid != nullptr;
+  hb.m = __builtin_amdgcn_make_buffer_rsrc((void*)(hb.has_mask ? a.kv_valid : kbh), 0,
+                                           hb.has_mask ? a.N : 0, kRsrcWord3);
+  hb.blk_k = MX ? 1 : a.blk_k;
+  hb.c = __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? kbh : (const void*)(a.k_scale + (int64_t)bh * a.nblk_k)),
+                                           0, MX ? 0 : a.nblk_k * 4, kRsrcWord3);
+
+  int k_off[MX ? 2 : QI];
+  if (MX) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) k_off[i] = lr * TL::KROW + 16 * ((2 * i + lg) ^ swz<4>(lr));
+  } else {
+#pragma unroll
+    for (int i = 0; i < QI; ++i) k_off[i] = lr * TL::KROW + 16 * ((QI * lg + i) ^ swz<TL::K_CPR>(lr));
+  }
+  const int v_off0 = lr * kBN + 16 * ((2 * lg) ^ swz<4>(lr));
+  const int v_off1 = lr * kBN + 16 * ((2 * lg + 1) ^ swz<4>(lr));
+
+  // K(t+3), V(t+2) and the side data of tile t+2 into the stages of tile
+  // t+3 and t+2 (r = t % 4); tiles past the end read zeros or in-bounds bytes
+  // of the same head into stages that are never read
+  auto issue_copies = [&](int t, int r) __attribute__((always_inline)) {
+    pp_issue_k<MX>(KS[(r + 3) & 3], hb, (t + 3) * kBN, wave, lane, kp);
+    pp_issue_v<MX>(VS[(r + 2) & 3], hb, a.n_alloc, (t + 2) * kBN, wave, vp);
+    issue_aux<D, MX>(XS[(r + 2) & 3], hb, (t + 2) * kBN, lane);
+  };
+
+  // S^T (keys x queries) of the tile in K stage Ks
+  auto qk = [&](const uint8_t* Ks, v16f (&s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      v16f acc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+      if (MX) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          v8i kr = {0, 0, 0, 0, 0, 0, 0, 0};
+          const uint4 x = *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]);
+          kr[0] = x.x; kr[1] = x.y; kr[2] = x.z; kr[3] = x.w;
+          const int ksc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], acc, 4, 4, 0, ksc, 0,
+                                                                qsc[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < QI; ++i) {
+          const v8s kr = __builtin_bit_cast(
+              v8s, *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qop16[i], acc, 0, 0, 0);
+        }
+      }
+      s[kb] = acc;
+    }
+  };
+  auto pv = [&](const uint8_t* Vs, const v8i& pk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+      const v8i vr = make_v8(*reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off0),
+                             *reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off1));
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vr, pk, o[cb], 0, 0, 0, 127, 0, 127);
+    }
+  };
+  // matrix phase t: O^T += V(t)^T P~(t)^T (V stage Vs), then S(t+1) (K stage Kn).
+  // The MFMAs are issued in order with their LDS operands read MLA MFMAs
+  // ahead (pinned with empty volatile asm), which bounds the registers held
+  // by operands in flight.  After the last tile S(t+1) is computed from a
+  // stage holding a copy past the end and never used, which keeps the phase
+  // free of branches.
+  constexpr int QPB = MX ? 2 : QI;
+  constexpr int NMM = DB + 2 * QPB;
+  constexpr int MLA = 4;
+  struct MOp { v8i a; int sc; };
+  auto mphase = [&](const int t, const uint8_t* Vs, const uint8_t* Kn, const v8i& pk, v16f (&s_out)[2])
+      __attribute__((always_inline)) {
+    auto read = [&](const int m, MOp& op) __attribute__((always_inline)) {
+      if (m < DB) {
+        op.a = make_v8(*reinterpret_cast<const uint4*>(Vs + m * 32 * kBN + v_off0),
+                       *reinterpret_cast<const uint4*>(Vs + m * 32 * kBN + v_off1));
+      } else {
+        const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
+        const uint4 x = *reinterpret_cast<const uint4*>(Kn + kb * 32 * TL::KROW + k_off[i]);
+        op.a[0] = x.x; op.a[1] = x.y; op.a[2] = x.z; op.a[3] = x.w;
+        if (MX) op.sc = Kn[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
+      }
+    };
+    MOp ops[NMM];
+    v16f acc[2];
+#pragma unroll
+    for (int m = 0; m < MLA; ++m) read(m, ops[m]);
+#pragma unroll
+    for (int m = 0; m < NMM; ++m) {
+      asm volatile("" : "+v"(ops[m].a));
+      if (m < DB) {
+        o[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ops[m].a, pk, o[m], 0, 0, 0, 127, 0, 127);
+      } else {
+        const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
+        v16f c0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c0[j] = 0.0f;
+        if (MX) {
+          v8i kr = {0, 0, 0, 0, 0, 0, 0, 0};
+          kr[0] = ops[m].a[0]; kr[1] = ops[m].a[1]; kr[2] = ops[m].a[2]; kr[3] = ops[m].a[3];
+          acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], i == 0 ? c0 : acc[kb],
+                                                                    4, 4, 0, ops[m].sc, 0, qsc[i]);
+        } else {
+          const v4i x = {ops[m].a[0], ops[m].a[1], ops[m].a[2], ops[m].a[3]};
+          acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8s, x), qop16[i],
+                                                            i == 0 ? c0 : acc[kb], 0, 0, 0);
+        }
+      }
+      if (m + MLA < NMM) read(m + MLA, ops[m + MLA]);
+    }
+    s_out[0] = acc[0];
+    s_out[1] = acc[1];
+    // the phase ends here: its MFMAs may not drift past the barrier into the
+    // vector phase (they would then compete with the other wave's MFMAs)
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) asm volatile("" : "+v"(o[cb]));
+    asm volatile("" : "+v"(s_out[0]), "+v"(s_out[1]));
+  };
+  // vector phase t: masks, running max, P~(t), row sums, rescale of O
+  auto vphase = [&](const int t, const uint8_t* Ar, v16f (&s)[2], v8i& pk) __attribute__((always_inline)) {
+    const int ks = t * kBN;
+    const float* Cs = reinterpret_cast<const float*>(Ar + TL::M_BYTES);
+    float c[8];
+    if (MX) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) c[g] = cq;
+    } else if (UK) {
+      const float ck = cq * __builtin_amdgcn_rcpf(Cs[0]);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) c[g] = ck;
+    } else {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int key = ks + 32 * (g / 4) + 8 * (g % 4);
+        c[g] = cq * __builtin_amdgcn_rcpf(Cs[key / a.blk_k - ks / a.blk_k]);
+      }
+    }
+    const bool edge = (ks + kBN > a.N) || (MODE == 1 && ks + kBN - 1 > wq0);
+    if (edge || hb.has_mask) {
+      const bool partial = hb.has_mask && Ar[lane] == 0;
+      if (edge || __builtin_amdgcn_ballot_w64(partial) != 0) {
+        const int lim = MODE == 1 ? min(a.N - 1, myq) : a.N - 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const uint32_t w = hb.has_mask
+                ? *reinterpret_cast<const uint32_t*>(Ar + 32 * kb + 8 * g4 + 4 * lg) : 0x01010101u;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int key = ks + 32 * kb + 8 * g4 + 4 * lg + jj;
+              const bool ok = (key <= lim) & (((w >> (8 * jj)) & 0xFFu) != 0u);
+              s[kb][4 * g4 + jj] = ok ? s[kb][4 * g4 + jj] : kNegInf;
+            }
+          }
+      }
+    }
+    float mx;
+    if (MX || UK) {
+      float m11[11];
+#pragma unroll
+      for (int i = 0; i < 10; ++i) {
+        const int e = 3 * i;
+        m11[i] = max3f(s[e / 16][e % 16], s[(e + 1) / 16][(e + 1) % 16], s[(e + 2) / 16][(e + 2) % 16]);
+      }
+      m11[10] = fmaxf(s[1][14], s[1][15]);
+      const float m = max3f(max3f(m11[0], m11[1], m11[2]), max3f(m11[3], m11[4], m11[5]),
+                            max3f(max3f(m11[6], m11[7], m11[8]), m11[9], m11[10]));
+      mx = c[0] * m;
+    } else {
+      mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float m4 = fmaxf(fmaxf(s[kb][4 * g4], s[kb][4 * g4 + 1]),
+                                 fmaxf(s[kb][4 * g4 + 2], s[kb][4 * g4 + 3]));
+          mx = fmaxf(mx, c[4 * kb + g4] * m4);
+        }
+    }
+    mx = swap_max(mx);
+    const float mnew = fmaxf(m_run, mx);
+    const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
+    const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448;
+    m_run = mnew;
+    float gs[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int kb = g / 4, g4 = g % 4;
+      const float cc = c[g];
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * g4 + j], cc, -msh));
+      gs[g] = (p[0] + p[1]) + (p[2] + p[3]);
+      int w;
+      asm volatile("" : "=v"(w));   // the two conversions below write all four bytes
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], w, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+      pk[g] = w;
+    }
+    const float sum = ((gs[0] + gs[1]) + (gs[2] + gs[3])) + ((gs[4] + gs[5]) + (gs[6] + gs[7]));
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha;
+    }
+    l_run = l_run * alpha + sum;
+    // likewise the vector work stays in its phase
+    asm volatile("" : "+v"(pk), "+v"(l_run));
+  };
+
+  // ---- prologue: K(0..2), V(0..1), side data of tiles 0 and 1; S(0)
+#pragma unroll
+  for (int t = 0; t < 3; ++t) pp_issue_k<MX>(KS[t], hb, t * kBN, wave, lane, kp);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    pp_issue_v<MX>(VS[t], hb, a.n_alloc, t * kBN, wave, vp);
+    issue_aux<D, MX>(XS[t], hb, t * kBN, lane);
+  }
+  wait_vm_le<0>();
+  barrier_lds();
+  v16f sa[2], sb[2];
+  v8i pa, pb;
+  qk(KS[0], sa);
+
+  // iteration t (r = t % 4, a constant in every unrolled copy); S(t) and
+  // P~(t) live in the buffers of parity t.  Both groups run the same
+  // sequence; group 1 starts one barrier late, which makes its vector phases
+  // coincide with group 0's matrix phases.  Copies issued in one iteration
+  // have landed for every wave by the end of the next one (each wave waits
+  // for its own, then the barrier), which is before their first use.
+  auto iteration = [&](const int t, const int r, v16f (&s_t)[2], v16f (&s_t1)[2], v8i& p_t)
+      __attribute__((always_inline)) {
+    vphase(t, XS[r], s_t, p_t);
+    barrier_lds();
+    issue_copies(t, r);
+    mphase(t, VS[r], KS[(r + 1) & 3], p_t, s_t1);
+    wait_vm_le<P::ISSUES>();
+    barrier_lds();
+  };
+  if (grp == 1) barrier_lds();
+  for (int t = 0; t < n_steps; t += 4) {
+    iteration(t, 0, sa, sb, pa);
+    if (t + 1 < n_steps) iteration(t + 1, 1, sb, sa, pb);
+    if (t + 2 < n_steps) iteration(t + 2, 2, sa, sb, pa);
+    if (t + 3 < n_steps) iteration(t + 3, 3, sb, sa, pb);
+  }
+  // keep the last P.V MFMAs here, with every lane active (see the store below)
+#pragma unroll
+  for (int cb = 0; cb < DB; ++cb) asm volatile("" : "+v"(o[cb]));
+  wait_vm_le<0>();
+
+  const float lt = swap_sum(l_run);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (myq < a.N) {
+    const int tok = a.out_perm ? a.out_perm[myq] : myq;
+    if (tok >= 0) {
+      const int b = bh / a.H, h = bh % a.H;
+      float* orow = a.out + b * a.osb + h * a.osh + (int64_t)tok * a.osn;
+      const float* vs = a.v_scale + (int64_t)bh * D;
+#pragma unroll
+      for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int c0 = 32 * cb + 8 * g4 + 4 * lg;
+          float4 r;
+          r.x = o[cb][4 * g4 + 0] * inv / vs[c0 + 0];
+          r.y = o[cb][4 * g4 + 1] * inv / vs[c0 + 1];
+          r.z = o[cb][4 * g4 + 2] * inv / vs[c0 + 2];
+          r.w = o[cb][4 * g4 + 3] * inv / vs[c0 + 3];
+          *reinterpret_cast<float4*>(orow + c0) = r;
+        }
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 template <int D, bool MX, int MODE>
 static hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const bool uk = MX || a.blk_k % kBN == 0;
@@ -659,7 +1087,22 @@ static hipError_t launch_mode(const AttnArgs& a, int mode, hipStream_t st) {
   return launch_t<D, MX, 0>(a, st);
 }
 
+template <bool MX, int MODE>
+static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
+  const bool uk = MX || a.blk_k % kBN == 0;
+  const int64_t blocks = (int64_t)a.B * a.H * ((a.n_alloc + PP<MX>::BMW - 1) / PP<MX>::BMW);
+  if (uk)
+    hipLaunchKernelGGL((attn_pp_kernel<MX, MODE, true>), dim3((unsigned)blocks), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_pp_kernel<MX, MODE, false>), dim3((unsigned)blocks), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnArgs& a, int d, bool mx, int mode, hipStream_t st) {
+  // dense FP8 with d = 128: the ping-pong kernel (its matrix phase, with QK^T
+  // on the bf16 MFMA, is long enough to balance the vector phase; for MXFP4
+  // and for causal masks the 4-wave kernel measures faster)
+  if (!mx && d == 128 && mode == 0) return launch_pp<false, 0>(a, st);
   if (mx) return launch_mode<128, true>(a, mode, st);
   if (d == 64) return launch_mode<64, false>(a, mode, st);
   return launch_mode<128, false>(a, mode, st);

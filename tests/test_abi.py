@@ -31,7 +31,11 @@ def test_exports_every_declared_symbol(B):
 
 def test_token_alloc_and_info(B):
     assert B.token_alloc(1) == 128 and B.token_alloc(128) == 128 and B.token_alloc(129) == 256
-    assert B.attention_info("fp8_block", 128, 0) == (128, 64)
+    assert B.attention_info("fp8_block", 128, 0) == (256, 64)
+    assert B.attention_info("fp8_block", 128, 1) == (128, 64)
+    assert B.attention_info("fp8_block", 128, 2) == (128, 64)
+    assert B.attention_info("fp8_block", 64, 0) == (128, 64)
+    assert B.attention_info("mxfp4", 128, 0) == (128, 64)
     assert B.attention_info("mxfp4", 128, 1)[1] == 64
     with pytest.raises(B.PabError):
         B.attention_info("mxfp4", 64, 0)
