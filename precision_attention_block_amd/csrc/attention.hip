@@ -450,9 +450,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
                   const uint8_t* Ar, uint8_t* Aw, v16f (&s_cur)[2], v16f (&s_nxt)[2],
                   const v8i& pk_in, v8i& pk) __attribute__((always_inline)) {
     const int ks = step_start(t);
-    issue_k<D, MX>(Kw, hb, tile_at(t + 3), wave, lane, kp);
-    issue_v<D, MX>(Vw, hb, a.n_alloc, tile_at(t + 1), wave, vp);
-    issue_aux<D, MX>(Aw, hb, tile_at(t + 2), lane);
+    // this iteration's copies (K(t+3), V(t+1), side data of t+2) are issued
+    // one instruction per slot below: issued back to back by every wave they
+    // would queue up at the texture unit and stall the issuing waves
+    const int ks_k = tile_at(t + 3), ks_v = tile_at(t + 1), ks_a = tile_at(t + 2);
+    auto copy_item = [&](const int j) __attribute__((always_inline)) {
+      constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI, KPER = DmaPlan<TL::K_CPR>::PER;
+      if (j < TL::KI) {
+        const int inst = wave * TL::KI + j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(Kw + inst * 1024), 16,
+                                                 kp.off[inst % KPER], (ks_k + inst * KRPI) * TL::KROW, 0, 0);
+      } else if (MX && j == TL::KI) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(Kw + TL::K_BYTES), 4, 4 * lane,
+                                                 ks_k * (D / 32), 0, 0);
+      } else if (j < NK + TL::VI) {
+        const int inst = wave * TL::VI + (j - NK);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.v, (lds_void_t*)(Vw + inst * 1024), 16, vp.off[0],
+                                                 ks_v + inst * 16 * a.n_alloc, 0, 0);
+      } else if (j == NK + NV) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.m, (lds_void_t*)Aw, 4, 4 * lane, ks_a, 0, 0);
+      } else if (!MX && j == NK + NV + 1) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.c, (lds_void_t*)(Aw + TL::M_BYTES), 4, 4 * lane,
+                                                 (ks_a / hb.blk_k) * 4, 0, 0);
+      }
+    };
+    static_assert(NK + NV + NA <= 8, "one copy instruction per slot");
 
     // dequantisation factor c (log2 domain): c = sm_scale log2(e) / (s_Q s_K),
     // per group of 4 keys (kb, j / 4); constant over the tile when UK.
@@ -562,6 +584,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     };
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
+      copy_item(g);
 #pragma unroll
       for (int m = slot_lo(g); m < slot_lo(g + 1); ++m) {
         asm volatile("" : "+v"(ops[m].a));
@@ -807,13 +830,37 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   const int v_off0 = lr * kBN + 16 * ((2 * lg) ^ swz<4>(lr));
   const int v_off1 = lr * kBN + 16 * ((2 * lg + 1) ^ swz<4>(lr));
 
-  // K(t+3), V(t+2) and the side data of tile t+2 into the stages of tile
-  // t+3 and t+2 (r = t % 4); tiles past the end read zeros or in-bounds bytes
-  // of the same head into stages that are never read
-  auto issue_copies = [&](int t, int r) __attribute__((always_inline)) {
-    pp_issue_k<MX>(KS[(r + 3) & 3], hb, (t + 3) * kBN, wave, lane, kp);
-    pp_issue_v<MX>(VS[(r + 2) & 3], hb, a.n_alloc, (t + 2) * kBN, wave, vp);
-    issue_aux<D, MX>(XS[(r + 2) & 3], hb, (t + 2) * kBN, lane);
+  // Copy item j of iteration t (r = t % 4): this wave's shares of K(t+3) and
+  // V(t+2) and the side data of tile t+2, into the stages of tiles t+3 and t+2.
+  // Tiles past the end read zeros or in-bounds bytes of the same head into
+  // stages that are never read.  The items are spread over the matrix phase:
+  // issued back to back by every wave they would queue up at the texture
+  // unit and stall the issuing waves.
+  auto copy_item = [&](const int j, const int t, const int r) __attribute__((always_inline)) {
+    constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI, KPER = DmaPlan<TL::K_CPR>::PER;
+    uint8_t* kbuf = KS[(r + 3) & 3];
+    const int ks_k = (t + 3) * kBN, ks_a = (t + 2) * kBN;
+    if (j < P::KI8) {
+      if (MX) {
+        if (wave < 4)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + wave * 1024), 16,
+                                                   kp.off[wave % KPER], (ks_k + wave * KRPI) * TL::KROW, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(kbuf + TL::K_BYTES), 4, 4 * lane,
+                                                   ks_k * (D / 32), 0, 0);
+      } else {
+        const int inst = wave + 8 * j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16,
+                                                 kp.off[inst % KPER], (ks_k + inst * KRPI) * TL::KROW, 0, 0);
+      }
+    } else if (j == P::KI8) {
+      pp_issue_v<MX>(VS[(r + 2) & 3], hb, a.n_alloc, (t + 2) * kBN, wave, vp);
+    } else if (j == P::KI8 + 1) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.m, (lds_void_t*)XS[(r + 2) & 3], 4, 4 * lane, ks_a, 0, 0);
+    } else if (!MX && j == P::KI8 + 2) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.c, (lds_void_t*)(XS[(r + 2) & 3] + TL::M_BYTES), 4,
+                                               4 * lane, (ks_a / hb.blk_k) * 4, 0, 0);
+    }
   };
 
   // S^T (keys x queries) of the tile in K stage Ks
@@ -862,8 +909,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   constexpr int NMM = DB + 2 * QPB;
   constexpr int MLA = 4;
   struct MOp { v8i a; int sc; };
-  auto mphase = [&](const int t, const uint8_t* Vs, const uint8_t* Kn, const v8i& pk, v16f (&s_out)[2])
-      __attribute__((always_inline)) {
+  auto mphase = [&](const int t, const int r, const uint8_t* Vs, const uint8_t* Kn, const v8i& pk,
+                    v16f (&s_out)[2]) __attribute__((always_inline)) {
     auto read = [&](const int m, MOp& op) __attribute__((always_inline)) {
       if (m < DB) {
         op.a = make_v8(*reinterpret_cast<const uint4*>(Vs + m * 32 * kBN + v_off0),
@@ -879,8 +926,10 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
     v16f acc[2];
 #pragma unroll
     for (int m = 0; m < MLA; ++m) read(m, ops[m]);
+    constexpr int CSTEP = NMM / P::ISSUES;   // MFMAs between two copy items
 #pragma unroll
     for (int m = 0; m < NMM; ++m) {
+      if (m % CSTEP == 0 && m / CSTEP < P::ISSUES) copy_item(m / CSTEP, t, r);
       asm volatile("" : "+v"(ops[m].a));
       if (m < DB) {
         o[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ops[m].a, pk, o[m], 0, 0, 0, 127, 0, 127);
@@ -1026,8 +1075,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
       __attribute__((always_inline)) {
     vphase(t, XS[r], s_t, p_t);
     barrier_lds();
-    issue_copies(t, r);
-    mphase(t, VS[r], KS[(r + 1) & 3], p_t, s_t1);
+    mphase(t, r, VS[r], KS[(r + 1) & 3], p_t, s_t1);
     wait_vm_le<P::ISSUES>();
     barrier_lds();
   };
