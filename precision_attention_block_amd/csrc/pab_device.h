@@ -82,18 +82,6 @@ __device__ inline float fp8_scale(float amax) {
   return (amax == 0.0f || !isfinite(s)) ? 1.0f : s;
 }
 
-// ---- FP4 E2M1 ----------------------------------------------------------------
-// Nearest grid point of |y| on {0, .5, 1, 1.5, 2, 3, 4, 6} with ties to the even
-// code, as a count of the decision thresholds passed: a tie at 0.25, 1.25, 2.5
-// or 5 stays on the lower (even) code, a tie at 0.75, 1.75 or 3.5 moves up to
-// the even code; everything above 5 saturates at 6 (code 7).
-__device__ inline uint32_t e2m1(float y) {
-  const float a = fabsf(y);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-               (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(y) >> 28) & 0x8u);
-}
-
 // ---- wave reductions -----------------------------------------------------------
 __device__ inline float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));

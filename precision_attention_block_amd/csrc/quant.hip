@@ -130,17 +130,28 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
 // until channel_finalize turns it into the scale.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void channel_amax_kernel(QuantArgs a) {
-  constexpr int TPR = D / 8, RPP = 256 / TPR, CHUNK = 256;
+  constexpr int TPR = D / 8, RPP = 256 / TPR, CHUNK = 256, ROUND = 256;
   const int bh = blockIdx.y, tid = threadIdx.x, col = (tid % TPR) * 8, r0 = tid / TPR;
   const int t0 = blockIdx.x * CHUNK;
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = r0; r < CHUNK; r += RPP) {
-    const int src = src_token(a, t0 + r);
-    if (src < 0) continue;
-    float w[8];
-    load8(token_ptr<T>(a, bh, src) + col, w);
+  // per round, all ROUND / RPP loads of a thread are issued before any is
+  // consumed
+  constexpr int NP = ROUND / RPP;
+  for (int r = 0; r < CHUNK; r += ROUND) {
+    Raw8<T> v[NP];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(w[j]));
+    for (int i = 0; i < NP; ++i) {
+      const int src = src_token(a, t0 + r + r0 + i * RPP);
+      if (src >= 0) v[i].load(token_ptr<T>(a, bh, src) + col);
+      else v[i].zero();
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      float w[8];
+      v[i].get(w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(w[j]));
+    }
   }
   __shared__ float red[RPP][D + 1];
 #pragma unroll
@@ -208,46 +219,61 @@ __global__ void channel_finalize_kernel(float* scales, int64_t n) {
 }
 
 // ------------------------------------------------------------ MXFP4
+// A thread owns 8 consecutive channels (a quarter of a 32-channel group) of 4
+// tokens: the lanes of a wave read 64 consecutive 16-byte chunks per load,
+// the four lanes of a group combine their amax with two quad permutes (DPP),
+// and every lane converts its 8 values with the hardware E2M1 conversion and
+// writes its 4 bytes of packed codes.
+__device__ inline float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  return v;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(QuantArgs a) {
-  constexpr int D = 128, NG = D / 32;
-  const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.H * a.n_alloc * NG;
-  if (gid >= total) return;
-  const int g = gid % NG;
-  const int64_t rowid = gid / NG;            // bh * n_alloc + token
-  const int tok = rowid % a.n_alloc;
-  const int bh = rowid / a.n_alloc;
-  const int src = src_token(a, tok);
-  float w[32];
-  if (src >= 0) {
-    const T* p = token_ptr<T>(a, bh, src) + 32 * g;
+  constexpr int D = 128, NG = D / 32, CPT = D / 8;   // chunks of 8 channels per token
+  constexpr int RPT = 4;                              // token rows per thread
+  // grid: x covers the n_alloc tokens of one (b, h) in groups of 64 (n_alloc
+  // is a multiple of 128, so every wave is whole and every lane reaches the
+  // permutes below), y is b * H + h
+  const int bh = blockIdx.y;
+  const int chunk = threadIdx.x % CPT, g = chunk / 4, sub = chunk % 4;
+  const int tok0 = blockIdx.x * 64 + threadIdx.x / CPT;
+  Raw8<T> v[RPT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float t[8];
-      load8(p + 8 * i, t);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w[8 * i + j] = t[j];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = 0.0f;
+  for (int i = 0; i < RPT; ++i) {
+    const int src = src_token(a, tok0 + 16 * i);
+    if (src >= 0) v[i].load(token_ptr<T>(a, bh, src) + 8 * chunk);
+    else v[i].zero();
   }
-  float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(w[i]));
-  // floor(log2 amax) from the exponent field; a zero or subnormal amax has
-  // floor(log2) <= -127, which the clamp maps to -127 either way.
-  const int e32 = (int)(__float_as_uint(amax) >> 23);
-  const int e = e32 == 0 ? -127 : max(e32 - 127 - 2, -127);
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
-  uint32_t packed[4] = {0, 0, 0, 0};
+  for (int i = 0; i < RPT; ++i) {
+    float w[8];
+    v[i].get(w);
+    float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i)
-    packed[i / 8] |= e2m1(__fmul_rn(w[i], inv)) << (4 * (i % 8));
-  uint8_t* out = a.codes + rowid * (D / 2) + 16 * g;
-  *reinterpret_cast<uint4*>(out) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  a.scales_u8[rowid * NG + g] = (uint8_t)(e + 127);
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(w[j]));
+    amax = quad_max(amax);
+    // floor(log2 amax) from the exponent field; a zero or subnormal amax has
+    // floor(log2) <= -127, which the clamp maps to -127 either way.
+    const int e32 = (int)(__float_as_uint(amax) >> 23);
+    const int e = e32 == 0 ? -127 : max(e32 - 127 - 2, -127);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
+    // the hardware E2M1 conversion (round to nearest even on the code, which
+    // is the tie rule of the recipe; |x / 2^e| < 8 saturates to 6); two
+    // elements per byte, element 2k in the low nibble
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = __fmul_rn(w[j], inv);
+    uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], 1.0f, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], 1.0f, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], 1.0f, 3);
+    const int64_t rowid = (int64_t)bh * a.n_alloc + tok0 + 16 * i;
+    *reinterpret_cast<uint32_t*>(a.codes + rowid * (D / 2) + 4 * chunk) = packed;
+    if (sub == 0) a.scales_u8[rowid * NG + g] = (uint8_t)(e + 127);
+  }
 }
 
 // ------------------------------------------------------------ non-finite count
@@ -285,9 +311,8 @@ static hipError_t launch_channel(const QuantArgs& a, hipStream_t st) {
 
 template <typename T>
 static hipError_t launch_mxfp4(const QuantArgs& a, hipStream_t st) {
-  const int64_t total = (int64_t)a.B * a.H * a.n_alloc * 4;
-  hipLaunchKernelGGL((quant_mxfp4_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     st, a);
+  const dim3 grid((unsigned)(a.n_alloc / 64), (unsigned)(a.B * a.H));   // n_alloc % 128 == 0
+  hipLaunchKernelGGL((quant_mxfp4_kernel<T>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
