@@ -61,3 +61,25 @@ def assert_close(got, ref, what=""):
     assert np.all(np.isfinite(got)), what + ": non-finite output"
     assert mx <= MAX_ABS and mean <= MEAN_ABS, "%s: max-abs %.3g mean-abs %.3g" % (what, mx, mean)
     return mx, mean
+
+
+def oracle_sta(x, grid, real_grid, tile, window, blk, bn, sm_scale):
+    """Oracle sliding-tile attention of raster-order inputs x = (q, k, v)
+    [B, H, N_real, d]: tokens regrouped tile-major, FP8 Q/K per blk-token
+    block, key tiles of each query tile from its window list; returns
+    [B, H, N_real, d] in raster order."""
+    op = OS.plan(grid, real_grid, tile, window)
+    q, k, v = (OS.gather_tokens(a, op.perm) for a in x)
+    B, H = q.shape[:2]
+    ops = oracle_operands(q, k, v, "fp8", blk)
+    ref = np.zeros(x[0].shape, np.float32)
+    for b in range(B):
+        for h in range(H):
+            qo, ko, vo = ops[b][h]
+            for u in range(op.n_tiles):
+                rows = np.arange(u * op.tile_tokens, (u + 1) * op.tile_tokens)
+                o = OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm_scale, bn=bn, kv_valid=op.kv_valid,
+                                        key_blocks=OS.key_blocks_for_tile(op, u, bn))
+                keep = op.perm[rows] >= 0
+                ref[b, h, op.perm[rows][keep]] = o[keep]
+    return ref

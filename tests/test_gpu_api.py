@@ -8,9 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention as OA
-from oracle import sta as OS
-from tests.helpers import assert_close, oracle_operands
+from tests.helpers import assert_close, oracle_sta
 from tests.test_gpu_attention import _inputs, _oracle_dense
 
 pytestmark = pytest.mark.gpu
@@ -47,19 +45,8 @@ def test_sta_through_device_plan(gpu_lib):
     n_real = int(np.prod(real))
     x, ts = _inputs(1, 2, n_real, 128, 91, torch.bfloat16, True)
     got = api.attention(*(t.cuda() for t in ts), recipe="fp8", block_tokens=None, sta=dp).cpu().numpy()
-    op = OS.plan(grid, real, tile, window)
     _, bn = gpu_lib.attention_info("fp8_block", 128, 2)
-    ref = np.zeros_like(got)
-    q, k, v = (OS.gather_tokens(a, op.perm) for a in x)
-    ops = oracle_operands(q, k, v, "fp8", op.tile_tokens)
-    for h in range(2):
-        qo, ko, vo = ops[0][h]
-        for u in range(op.n_tiles):
-            rows = np.arange(u * op.tile_tokens, (u + 1) * op.tile_tokens)
-            o = OA.recipe_attention(qo, ko, vo, rows, sm_scale=1 / np.sqrt(128), bn=bn,
-                                    kv_valid=op.kv_valid, key_blocks=OS.key_blocks_for_tile(op, u, bn))
-            keep = op.perm[rows] >= 0
-            ref[0, h, op.perm[rows][keep]] = o[keep]
+    ref = oracle_sta(x, grid, real, tile, window, hp.tile_tokens, bn, 1 / np.sqrt(128))
     assert_close(got, ref, "api sta")
 
 
