@@ -258,7 +258,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
   const int wq0 = q0 + wave * 32;             // first query of this wave
   const int myq = wq0 + lr;                   // this lane's query
-  const int32_t* wlist = MODE == 2 ? a.win_idx + a.win_off[u] : nullptr;
+  // The window list does not change during the launch: read through the
+  // constant address space its entries become scalar loads, whose completion
+  // counter is not the one the tile copies count on (a vector load would make
+  // every step wait for the copies issued before it).
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* wlist = MODE == 2 ? (const_i32*)(a.win_idx + a.win_off[u]) : nullptr;
   auto step_start = [&](int t) -> int {
     if (MODE == 2) return wlist[t / spt] * a.tile_tokens + (t % spt) * kBN;
     return t * kBN;
