@@ -100,7 +100,7 @@ pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, in
  *          contiguous.  If NULL, n_out must equal N_in and token p is input
  *          token p.
  * block_tokens  tokens per scale block for PAB_FP8_TOKEN_BLOCK (a multiple of
- *          16, at most 1024); ignored otherwise.
+ *          16, at most 16384); ignored otherwise.
  * Outputs (n_alloc = pab_token_alloc(n_out)):
  *  PAB_FP8_TOKEN_BLOCK: codes uint8 [B, H, n_alloc, d];
  *                       scales float32 [B, H, ceil(n_alloc / block_tokens)]

@@ -50,7 +50,7 @@ pab_status check_view(const pab_qview* v, int role) {
   }
   if (v->recipe == PAB_FP8_TOKEN_BLOCK) {
     if (v->d != 64 && v->d != 128) return PAB_UNSUPPORTED;
-    if (v->block_tokens < 16 || v->block_tokens > 1024 || v->block_tokens % 16) return PAB_INVALID_ARG;
+    if (v->block_tokens < 16 || v->block_tokens > 16384 || v->block_tokens % 16) return PAB_INVALID_ARG;
     if (!v->operand || !aligned(v->operand, 16)) return PAB_INVALID_ARG;
     return PAB_OK;
   }
@@ -170,7 +170,7 @@ pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
   if (B * H > (int64_t)1 << 24 || n_out > (int64_t)1 << 28 || N > (int64_t)1 << 31) return PAB_UNSUPPORTED;
   if (recipe == PAB_FP8_TOKEN_BLOCK) {
     if (d != 64 && d != 128) return PAB_UNSUPPORTED;
-    if (block_tokens < 16 || block_tokens > 1024 || block_tokens % 16) return PAB_INVALID_ARG;
+    if (block_tokens < 16 || block_tokens > 16384 || block_tokens % 16) return PAB_INVALID_ARG;
   } else if (recipe == PAB_FP8_CHANNEL) {
     if (d != 64 && d != 128) return PAB_UNSUPPORTED;
   } else if (recipe == PAB_MXFP4_D32) {

@@ -79,7 +79,7 @@ def test_quantize_validation_without_device(B):
     assert q(fake, 7, shape, strides, 0, 128, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
     assert q(fake, 1, shape, strides, 9, 128, null, 256, fake, fake, null, null) == B.PAB_INVALID_ARG
     assert q(fake, 1, shape, strides, 0, 100, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
-    assert q(fake, 1, shape, strides, 0, 2048, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
+    assert q(fake, 1, shape, strides, 0, 16400, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG
     assert q(fake, 1, shape, strides, 0, 128, null, 300, fake, fake, fake, null) == B.PAB_INVALID_ARG
     bad_str = B._i64([2 * 256 * 128, 256 * 128, 128, 2])
     assert q(fake, 1, shape, bad_str, 0, 128, null, 256, fake, fake, fake, null) == B.PAB_INVALID_ARG

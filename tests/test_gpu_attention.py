@@ -138,6 +138,37 @@ def test_sta_parity_with_padding(gpu_lib, window):
     assert_close(got, ref, "sta %s" % (window,))
 
 
+@pytest.mark.parametrize("grid,real,tile,window", [
+    ((8, 16, 24), (7, 15, 22), (4, 8, 8), (3, 3, 3)),          # 256-token tiles
+    ((6, 32, 32), (5, 30, 31), (6, 16, 16), (1, 3, 3)),        # 1536-token tiles
+])
+def test_sta_tile_variants(gpu_lib, grid, real, tile, window):
+    """Other tile shapes of the sliding-tile schedule (the FPSAttention page,
+    tile-size ablation): per-tile FP8 scales over 256 and 1536 tokens, padded
+    grids; 96 sampled query rows per tile (first, last and seeded ones)."""
+    hp, op, x, ts = _sta_setup(gpu_lib, grid, real, tile, window, seed=43)
+    got = _run_sta(gpu_lib, hp, ts)
+    _, bn = gpu_lib.attention_info("fp8_block", 128, 2)
+    xk = [OS.gather_tokens(a, op.perm) for a in x]
+    ops = oracle_operands(*xk, "fp8", op.tile_tokens)
+    tt = op.tile_tokens
+    rng = np.random.default_rng(7)
+    checked = 0
+    for h in range(2):
+        qo, ko, vo = ops[0][h]
+        for u in range(op.n_tiles):
+            rows = np.unique(np.concatenate([[0, tt - 1], rng.choice(tt, 94, replace=False)])) + u * tt
+            rows = rows[op.perm[rows] >= 0]
+            if rows.size == 0:
+                continue
+            o = OA.recipe_attention(qo, ko, vo, rows, sm_scale=1 / np.sqrt(128), bn=bn,
+                                    kv_valid=op.kv_valid,
+                                    key_blocks=OS.key_blocks_for_tile(op, u, bn))
+            assert_close(got[0, h, op.perm[rows]], o, "sta tile %s head %d tile %d" % (tile, h, u))
+            checked += rows.size
+    assert checked > 0
+
+
 def test_sta_full_window_equals_dense_bitwise(gpu_lib):
     grid, real, tile = (4, 16, 16), (4, 13, 16), (2, 8, 8)
     hp, op, x, ts = _sta_setup(gpu_lib, grid, real, tile, (9, 9, 9), seed=41)

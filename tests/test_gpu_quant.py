@@ -24,7 +24,8 @@ def _inputs(shape, seed, dtype, outliers=True):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("B,H,N,d,blk", [(1, 2, 256, 64, 64), (1, 3, 1000, 128, 128),
-                                          (2, 2, 200, 128, 384), (1, 1, 77, 64, 16)])
+                                          (2, 2, 200, 128, 384), (1, 1, 77, 64, 16),
+                                          (1, 2, 3500, 128, 1536), (1, 1, 700, 64, 2048)])
 def test_fp8_block_bit_exact(gpu_lib, dtype, B, H, N, d, blk):
     print("fp8_block", B, H, N, d, blk, dtype, flush=True)
     x, xt = _inputs((B, H, N, d), 100 + N, dtype)
