@@ -5,27 +5,34 @@ Definition [FV §2.1]: Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V.
 FlashAttention [FA4, FlashAttention section]: the keys are visited tile by tile
 and the softmax is normalised while it is computed (online softmax), so no
 N x N matrix is kept.  [FA4, co-design list: conditional softmax rescaling]
-the running output is rescaled only when the running maximum moves; with a
-threshold of zero this changes nothing numerically (a factor of exactly 1),
-so the recipe below rescales unconditionally.
+the running output is rescaled only when the running maximum crosses a
+threshold.  With threshold tau = 0 (the default recipe) the reference maximum
+follows every rise and a skipped rescale is a factor of exactly 1.  With
+tau > 0 (log2 units, an integer) the reference maximum moves only when a row
+maximum exceeds it by more than tau, so P may reach 2^tau; P is then
+quantised with the scale 448 / 2^tau, which keeps it inside the E4M3 range.
 [FPS §3.1] P is quantised per tensor to FP8 with the fixed scale 1/448:
-P~ = E4M3(448 * P) and P ~= P~ / 448.
+P~ = E4M3(448 * P) and P ~= P~ / 448 (tau = 0).
 
 Recipe, one query row i of one (batch, head), key tiles of BN keys visited in
 ascending order (for sliding-tile attention: the tiles of the query's window
 list in ascending order; causal: keys j <= i; padded keys masked):
-  m = -inf, l = 0, acc = 0
+  m = -inf, l = 0, acc = 0, rho = 448 / 2^tau
   per tile:
     S_j   = fl32( (sum_k dec(qQ_ik) dec(qK_jk)) / (s_Q(i) s_K(j)) * sm_scale * log2(e) )
             (MXFP4: the per-32 scales 2^(eQ+eK) sit inside the sum);
             masked keys get S_j = -inf; a tile without a valid key is skipped
-    m'    = max(m, max_j S_j);   alpha = 2^(m - m')  (1 when m' == m)
-    P_j   = fl32(2^(S_j - m'))                      (so 0 <= P_j <= 1)
+    c     = max(m, max_j S_j)
+    m'    = c if c > fl32(m + tau) else m   (tau = 0: m' = c)
+    alpha = 2^(m - m')  (1 when m' == m)
+    P_j   = fl32(2^(S_j - m'))                      (so 0 <= P_j <= 2^tau)
     l     = alpha l + sum_j P_j                      (P before quantisation)
-    P~_j  = E4M3(fl32(448 P_j))
+    P~_j  = E4M3(fl32(rho P_j))
     acc_c = alpha acc_c + sum_j dec(P~_j) dec(qV_jc) (float64)
     m     = m'
-  O_ic = fl32(acc_c / l / 448 / s_V(c)); a row with no valid key gives 0.
+  O_ic = fl32(acc_c / l / rho / s_V(c)); a row with no valid key gives 0.
+(The comparison c > m + tau decides whether the reference moves; it is made
+in float32, as in the kernel.)
 The products of decoded FP8 codes are exact in float64 and so are their sums
 at these lengths, so a float64 matrix product serves as the exact sum.
 """
@@ -74,14 +81,18 @@ def scores(q, k, qrows, kcols, sm_scale, fp64_core=False):
 
 
 def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None,
-                     key_blocks=None, quantize_p=True, fp64_core=False):
+                     key_blocks=None, quantize_p=True, fp64_core=False, tau=0):
     """Output rows O[rows, :] (float32) of one (batch, head).
 
     key_blocks: None (all BN-key tiles 0..ceil(N/BN)-1) or an ascending list of
     key-tile start indices shared by every row in `rows`.
+    tau: rescale threshold (integer, log2 units; 0 = the eager recipe).
     quantize_p=False / fp64_core=True switch parts of the recipe off so that
     tests can pin the online-softmax core against the brute force.
     """
+    if int(tau) != tau or tau < 0:
+        raise ValueError("tau must be a non-negative integer")
+    p_scale = 448.0 * 2.0 ** -int(tau)
     rows = np.asarray(rows, dtype=np.int64)
     n, d = k.codes.shape
     r = len(rows)
@@ -102,7 +113,9 @@ def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None
         s = np.where(valid, s, -np.inf).astype(ftype)
         tmax = s.max(axis=1)
         has = valid.any(axis=1)
-        m_new = np.where(has, np.maximum(m, tmax), m).astype(ftype)
+        cand = np.where(has, np.maximum(m, tmax), m).astype(ftype)
+        moves = cand > (m + ftype(tau)).astype(ftype)     # -inf + tau stays -inf
+        m_new = np.where(moves, cand, m).astype(ftype)
         with np.errstate(invalid="ignore"):
             alpha = np.where(m_new == m, 1.0,
                              np.exp2(m.astype(np.float64) - m_new.astype(np.float64)))
@@ -112,13 +125,13 @@ def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None
             p = p.astype(np.float32)
         l = alpha * l + p.astype(np.float64).sum(axis=1)
         if quantize_p:
-            pq = e4m3_decode(e4m3_encode(np.float32(448.0) * p.astype(np.float32)))
+            pq = e4m3_decode(e4m3_encode(np.float32(p_scale) * p.astype(np.float32)))
         else:
-            pq = 448.0 * p.astype(np.float64)
+            pq = p_scale * p.astype(np.float64)
         acc = alpha[:, None] * acc + pq @ e4m3_decode(v.codes[cols])
         m = m_new
     with np.errstate(invalid="ignore", divide="ignore"):
-        o = acc / l[:, None] / 448.0 / v.scales.astype(np.float64)[None, :]
+        o = acc / l[:, None] / p_scale / v.scales.astype(np.float64)[None, :]
     o = np.where((l > 0)[:, None], o, 0.0)
     return o.astype(np.float32)
 

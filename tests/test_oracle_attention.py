@@ -191,3 +191,52 @@ def test_sta_full_window_is_dense_bitwise_and_radius_zero_is_per_tile():
         vs = A.Operand("fp8_channel", vo.codes[sub], vo.scales)
         alone = A.recipe_attention(qs, ks, vs, np.arange(tt), sm_scale=0.2, bn=16)
         assert np.array_equal(zero, alone)
+
+
+@pytest.mark.parametrize("tau", [1, 3, 8])
+@pytest.mark.parametrize("recipe", ["fp8", "mxfp4"])
+def test_lazy_rescale_core_equals_brute_force(recipe, tau):
+    """A rescale threshold tau > 0 only delays the change of reference
+    maximum, which the normaliser and the accumulator share: with P not
+    quantised the online softmax still equals the brute force exactly."""
+    q, k, v = _rand(160, 64, 12, 2.0)
+    k = k * np.linspace(0.5, 2.5, 160, dtype=np.float32)[:, None]   # maxima keep rising
+    qo, ko, vo, qh, kh, vh = _ops(q, k, v, recipe=recipe)
+    sm = 1 / np.sqrt(64)
+    o = A.recipe_attention(qo, ko, vo, np.arange(160), sm_scale=sm, bn=16, quantize_p=False,
+                           fp64_core=True, tau=tau)
+    assert np.allclose(o, A.brute_force(qh, kh, vh, sm), rtol=2e-7, atol=1e-7)
+
+
+def test_lazy_rescale_worked_case():
+    """Two one-key tiles with logits 0 and 1.5 (log2 units), V = identity rows.
+    tau = 0 and tau = 1: the reference maximum moves to 1.5, every P~ is exact
+    (448 and 224 are E4M3 values), the output is the exact softmax.
+    tau = 2: the reference stays at 0, P = (1, 2^1.5), P~ = E4M3(112 P) =
+    (112, 320) (316.8 rounds to 320 on the E4M3 grid), so
+    O = (112, 320) / 112 / (1 + 2^1.5)."""
+    d = 32
+    q = np.zeros((1, d), np.float32); q[0, 0] = 1.0
+    k = np.zeros((2, d), np.float32); k[1, 0] = 1.0
+    v = np.zeros((2, d), np.float32); v[0, 0] = 1.0; v[1, 1] = 1.0
+    qo, ko, vo, *_ = _ops(q, k, v, blk=2)
+    sm = 1.5 / A.LOG2E
+    w = 2.0 ** -1.5
+    exact = np.array([w / (1 + w), 1 / (1 + w)])
+    for tau in (0, 1):
+        o = A.recipe_attention(qo, ko, vo, [0], sm_scale=sm, bn=1, tau=tau)[0]
+        assert np.allclose(o[:2], exact, rtol=1e-6), tau
+    o = A.recipe_attention(qo, ko, vo, [0], sm_scale=sm, bn=1, tau=2)[0]
+    p1 = float(np.float32(2.0 ** 1.5))
+    assert np.allclose(o[:2], np.array([112.0, 320.0]) / 112.0 / (1 + p1), rtol=1e-6)
+    assert np.all(o[2:] == 0)
+
+
+def test_lazy_rescale_tau_zero_is_the_default():
+    q, k, v = _rand(96, 64, 13, 2.0)
+    qo, ko, vo, *_ = _ops(q, k, v)
+    a = A.recipe_attention(qo, ko, vo, np.arange(96), sm_scale=0.125, bn=16)
+    b = A.recipe_attention(qo, ko, vo, np.arange(96), sm_scale=0.125, bn=16, tau=0)
+    assert np.array_equal(a, b)
+    with pytest.raises(ValueError):
+        A.recipe_attention(qo, ko, vo, [0], sm_scale=0.125, bn=16, tau=1.5)
