@@ -114,9 +114,9 @@ def roofline_peak(cfg):
 class GpuPath:
     """Device tensors and one step of the path through the C ABI."""
 
-    def __init__(self, cfg, x, lib):
+    def __init__(self, cfg, x, lib, tau=0):
         import torch
-        self.cfg, self.lib = cfg, lib
+        self.cfg, self.lib, self.tau = cfg, lib, tau
         dev = torch.device("cuda:0")
         self.q, self.k, self.v = (x[n].to(dev) for n in ("q_t", "k_t", "v_t"))
         self.plan = None
@@ -143,11 +143,13 @@ class GpuPath:
     def attend(self, qq, kq, vq):
         cfg, lib = self.cfg, self.lib
         if cfg.mode == "sta":
-            return lib.attention_sta(qq, kq, vq, self.dplan, out=self.out)
+            return lib.attention_sta(qq, kq, vq, self.dplan, out=self.out, tau=self.tau)
         if self.dplan is not None:
             return lib.attention_dense(qq, kq, vq, kv_valid=self.dplan.kv_valid,
-                                       out_perm=self.dplan.perm, n_out=cfg.n_real, out=self.out)
-        return lib.attention_dense(qq, kq, vq, causal=cfg.mode == "causal", out=self.out)
+                                       out_perm=self.dplan.perm, n_out=cfg.n_real, out=self.out,
+                                       tau=self.tau)
+        return lib.attention_dense(qq, kq, vq, causal=cfg.mode == "causal", out=self.out,
+                                   tau=self.tau)
 
 
 def time_gpu(path, steps, warmup):
@@ -239,6 +241,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--tau", type=int, default=0,
+                    help="softmax rescale threshold in log2 units (0 = rescale on every rise of "
+                         "the running maximum, the default recipe)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device copy of this many bytes "
                          "(counter calibration for rocprofv3 --pmc runs)")
@@ -257,7 +262,7 @@ def main():
     cfg = CONFIGS[args.config]
     print("[bench] config %s: generating inputs" % cfg.name, file=sys.stderr, flush=True)
     x = make_inputs(cfg, as_torch=True)
-    path = GpuPath(cfg, x, lib)
+    path = GpuPath(cfg, x, lib, args.tau)
     mode = {"dense": 0, "causal": 1, "sta": 2}[cfg.mode]
     _, bn = lib.attention_info("mxfp4" if cfg.recipe == "mxfp4" else "fp8_block", cfg.d, mode)
     print("[bench] timing %d steps after %d warm-up" % (args.steps, args.warmup), file=sys.stderr,
@@ -285,7 +290,7 @@ def main():
         "config": {"workload": cfg.name, "desc": cfg.desc, "B": cfg.B, "H": cfg.H,
                    "N": cfg.n_real, "N_kernel": cfg.n_kernel, "d": cfg.d, "mode": cfg.mode,
                    "recipe": cfg.recipe, "block_tokens": cfg.blk if cfg.recipe == "fp8" else 32,
-                   "BN": bn, "algorithmic_flops": flops,
+                   "BN": bn, "tau": args.tau, "algorithmic_flops": flops,
                    "dense_equivalent_flops": dense_equiv,
                    "quantize_ms": round(float(np.mean(q_ms)), 4),
                    "attention_ms": round(att_ms, 4),
@@ -295,7 +300,7 @@ def main():
                    "pct_fp4_peak": round(100 * achieved / PEAK_FP4, 2) if cfg.recipe == "mxfp4" else None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": recorded_traffic(cfg.name)},
+                     "traffic": recorded_traffic(cfg.name) if args.tau == 0 else None},
     }
     if args.copy_bytes > 0:
         copy_calibration(args.copy_bytes)

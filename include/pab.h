@@ -39,8 +39,9 @@
 extern "C" {
 #endif
 
-#define PAB_ABI_VERSION 1
+#define PAB_ABI_VERSION 2
 #define PAB_TOKEN_ALIGN 128  /* query tile of the attention kernel */
+#define PAB_MAX_TAU 8        /* largest softmax rescale threshold (log2 units) */
 
 typedef enum {
   PAB_OK = 0,
@@ -151,6 +152,15 @@ typedef struct {
  * FP8 matrix instructions.
  * O[i,c] = acc[i,c] / (448 l_i) / s_V[c]; a row with no valid key gives 0.
  * sm_scale <= 0 means 1/sqrt(d)  [FV §5.2 scaling_factor].
+ * tau       softmax rescale threshold, an integer in log2 units, 0 ..
+ *           PAB_MAX_TAU [FA4 co-design list: conditional rescaling]: the
+ *           reference maximum m of a row moves only when the row maximum
+ *           exceeds m + tau (a float32 comparison); until then P = 2^(S - m)
+ *           may reach 2^tau, and P~ = E4M3(448 / 2^tau * P), l and acc are
+ *           kept against the stale m (O divides by 448 / 2^tau instead of
+ *           448).  tau = 0 is the recipe above; a larger tau skips most
+ *           rescales of the accumulator at the cost of tau bits of P~ range
+ *           at the small end.  Out of range: PAB_INVALID_ARG.
  * kv_valid  device uint8 [N] or NULL: keys with 0 are masked (padding).
  * out_perm  device int32 [N] or NULL: query p is stored at output token
  *           out_perm[p] (skipped if -1); NULL stores query p at token p.
@@ -159,7 +169,7 @@ typedef struct {
  *           written.
  */
 pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab_qview* v,
-                               int causal, float sm_scale, const uint8_t* kv_valid,
+                               int causal, float sm_scale, int tau, const uint8_t* kv_valid,
                                const int32_t* out_perm, int64_t n_out_tokens, float* out,
                                const int64_t out_strides[4], void* stream);
 
@@ -177,7 +187,7 @@ pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab
  * tile_tokens.
  */
 pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_qview* v,
-                             float sm_scale, const int32_t* win_off, const int32_t* win_idx,
+                             float sm_scale, int tau, const int32_t* win_off, const int32_t* win_idx,
                              const int32_t* tile_order, int n_tiles, int tile_tokens,
                              const uint8_t* kv_valid, const int32_t* out_perm,
                              int64_t n_out_tokens, float* out, const int64_t out_strides[4],

@@ -23,21 +23,22 @@ def quantize_qkv(q, k, v, recipe="fp8", block_tokens=128, perm=None, n_out=None)
 
 
 def attention(q, k, v, recipe="fp8", block_tokens=128, causal=False, sm_scale=None, sta=None,
-              check_finite=False):
+              check_finite=False, tau=0):
     """q, k, v: CUDA tensors [B, H, N, d] (float32 or bfloat16, any strides with
     unit channel stride; a packed qkv [B, N, 3, H, d] can be passed as three
     permuted views).  sta: None, or a binding.DevicePlan for sliding-tile
     attention over tokens given in raster order of the plan's real grid.
+    tau: softmax rescale threshold (0 = rescale on every rise of the maximum).
     Returns float32 [B, H, N, d]."""
     if sta is None:
         qq, kq, vq = quantize_qkv(q, k, v, recipe, block_tokens)
-        out = B.attention_dense(qq, kq, vq, causal=causal, sm_scale=sm_scale)
+        out = B.attention_dense(qq, kq, vq, causal=causal, sm_scale=sm_scale, tau=tau)
     else:
         if causal:
             raise ValueError("sliding-tile attention has no causal mask")
         qq, kq, vq = quantize_qkv(q, k, v, recipe, sta.tile_tokens if block_tokens is None
                                   else block_tokens, sta.perm, sta.n_tokens)
-        out = B.attention_sta(qq, kq, vq, sta, sm_scale=sm_scale)
+        out = B.attention_sta(qq, kq, vq, sta, sm_scale=sm_scale, tau=tau)
     if check_finite:
         bad = int(B.count_nonfinite(out).item())
         if bad:

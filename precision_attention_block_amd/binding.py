@@ -68,11 +68,11 @@ def _lib():
                                    ctypes.c_int64, vp, vp, vp, vp]
         L.pab_attention_dense.restype = ctypes.c_int
         L.pab_attention_dense.argtypes = [ctypes.POINTER(QView)] * 3 + [
-            ctypes.c_int, ctypes.c_float, vp, vp, ctypes.c_int64, vp, i64p, vp]
+            ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, vp, ctypes.c_int64, vp, i64p, vp]
         L.pab_attention_sta.restype = ctypes.c_int
         L.pab_attention_sta.argtypes = [ctypes.POINTER(QView)] * 3 + [
-            ctypes.c_float, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int64, vp,
-            i64p, vp]
+            ctypes.c_float, ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp,
+            ctypes.c_int64, vp, i64p, vp]
         ip = ctypes.POINTER(ctypes.c_int)
         L.pab_sta_plan.restype = ctypes.c_int
         L.pab_sta_plan.argtypes = [ip, ip, ip, ip, vp, vp, vp, vp, vp, vp, i64p, i64p, i64p]
@@ -179,15 +179,16 @@ def _out_tensor(q, n_out, out):
 
 
 def attention_dense(q, k, v, causal=False, sm_scale=None, kv_valid=None, out_perm=None,
-                    n_out=None, out=None):
+                    n_out=None, out=None, tau=0):
     """O = softmax(Q K^T sm_scale) V on quantised operands; returns float32
-    [B, H, n_out, d] (n_out defaults to N)."""
+    [B, H, n_out, d] (n_out defaults to N).  tau: softmax rescale threshold
+    (see pab_attention_dense)."""
     n_out = q.N if n_out is None else int(n_out)
     out = _out_tensor(q, n_out, out)
     qv, kv, vv = q.view(), k.view(), v.view()
     st = _lib().pab_attention_dense(
         ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), int(bool(causal)),
-        float(sm_scale or 0.0),
+        float(sm_scale or 0.0), int(tau),
         ctypes.c_void_p(kv_valid.data_ptr() if kv_valid is not None else 0),
         ctypes.c_void_p(out_perm.data_ptr() if out_perm is not None else 0), n_out,
         ctypes.c_void_p(out.data_ptr()), _i64(out.stride()), _stream(out.device))
@@ -196,7 +197,7 @@ def attention_dense(q, k, v, causal=False, sm_scale=None, kv_valid=None, out_per
 
 
 def attention_sta(q, k, v, plan, sm_scale=None, use_kv_valid=True, use_out_perm=True, n_out=None,
-                  out=None):
+                  out=None, tau=0):
     """Sliding-tile attention with a DevicePlan (see sta_plan / DevicePlan)."""
     n_out = plan.n_real if n_out is None else int(n_out)
     if not use_out_perm and n_out is None:
@@ -204,7 +205,7 @@ def attention_sta(q, k, v, plan, sm_scale=None, use_kv_valid=True, use_out_perm=
     out = _out_tensor(q, n_out, out)
     qv, kv, vv = q.view(), k.view(), v.view()
     st = _lib().pab_attention_sta(
-        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(sm_scale or 0.0),
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(sm_scale or 0.0), int(tau),
         ctypes.c_void_p(plan.win_off.data_ptr()), ctypes.c_void_p(plan.win_idx.data_ptr()),
         ctypes.c_void_p(plan.lpt.data_ptr()), int(plan.n_tiles), int(plan.tile_tokens),
         ctypes.c_void_p(plan.kv_valid.data_ptr() if use_kv_valid else 0),

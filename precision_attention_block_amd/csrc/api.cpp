@@ -59,7 +59,7 @@ pab_status check_view(const pab_qview* v, int role) {
 }
 
 pab_status fill_attn_args(const pab_qview* q, const pab_qview* k, const pab_qview* v,
-                          float sm_scale, const uint8_t* kv_valid, const int32_t* out_perm,
+                          float sm_scale, int tau, const uint8_t* kv_valid, const int32_t* out_perm,
                           int64_t n_out_tokens, float* out, const int64_t out_strides[4],
                           pab::AttnArgs& a) {
   pab_status s;
@@ -78,6 +78,7 @@ pab_status fill_attn_args(const pab_qview* q, const pab_qview* k, const pab_qvie
   if (n_out_tokens < 1) return PAB_INVALID_ARG;
   if (!out_perm && n_out_tokens < q->N) return PAB_INVALID_ARG;
   if (kv_valid && !aligned(kv_valid, 4)) return PAB_INVALID_ARG;
+  if (tau < 0 || tau > PAB_MAX_TAU) return PAB_INVALID_ARG;
   if (!(std::isfinite(sm_scale))) return PAB_INVALID_ARG;
   const bool mx = q->recipe == PAB_MXFP4_D32;
   const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt((float)q->d);
@@ -112,6 +113,7 @@ pab_status fill_attn_args(const pab_qview* q, const pab_qview* k, const pab_qvie
     a.nblk_k = (int)((a.n_alloc + a.blk_k - 1) / a.blk_k);
   }
   a.sm_log2 = scale * 1.4426950408889634f;
+  a.tau = (float)tau;
   a.n_qtiles = a.n_alloc / pab::kBM;
   return PAB_OK;
 }
@@ -209,11 +211,11 @@ pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
 }
 
 pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab_qview* v,
-                               int causal, float sm_scale, const uint8_t* kv_valid,
+                               int causal, float sm_scale, int tau, const uint8_t* kv_valid,
                                const int32_t* out_perm, int64_t n_out_tokens, float* out,
                                const int64_t out_strides[4], void* stream) {
   pab::AttnArgs a;
-  pab_status s = fill_attn_args(q, k, v, sm_scale, kv_valid, out_perm, n_out_tokens, out,
+  pab_status s = fill_attn_args(q, k, v, sm_scale, tau, kv_valid, out_perm, n_out_tokens, out,
                                 out_strides, a);
   if (s != PAB_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -223,7 +225,7 @@ pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab
 }
 
 pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_qview* v,
-                             float sm_scale, const int32_t* win_off, const int32_t* win_idx,
+                             float sm_scale, int tau, const int32_t* win_off, const int32_t* win_idx,
                              const int32_t* tile_order, int n_tiles, int tile_tokens,
                              const uint8_t* kv_valid, const int32_t* out_perm,
                              int64_t n_out_tokens, float* out, const int64_t out_strides[4],
@@ -232,7 +234,7 @@ pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_q
   if (n_tiles < 1 || tile_tokens < PAB_TOKEN_ALIGN || tile_tokens % PAB_TOKEN_ALIGN)
     return PAB_INVALID_ARG;
   pab::AttnArgs a;
-  pab_status s = fill_attn_args(q, k, v, sm_scale, kv_valid, out_perm, n_out_tokens, out,
+  pab_status s = fill_attn_args(q, k, v, sm_scale, tau, kv_valid, out_perm, n_out_tokens, out,
                                 out_strides, a);
   if (s != PAB_OK) return s;
   if ((int64_t)n_tiles * tile_tokens != q->N) return PAB_INVALID_ARG;

@@ -562,9 +562,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         }
     }
     mx = swap_max(mx);
-    const float mnew = fmaxf(m_run, mx);
+    // the reference maximum moves only when the row maximum exceeds it by
+    // more than tau (tau = 0: on every rise); P = 2^(S c - m) <= 2^tau is
+    // quantised with the scale 448 / 2^tau
+    const float cand = fmaxf(m_run, mx);
+    const float mnew = cand > m_run + a.tau ? cand : m_run;
     const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
-    const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448;
+    const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448 + a.tau;
     m_run = mnew;
 
     // The previous tile's P.V and the next tile's S are independent MFMAs;
@@ -1027,9 +1031,13 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
         }
     }
     mx = swap_max(mx);
-    const float mnew = fmaxf(m_run, mx);
+    // the reference maximum moves only when the row maximum exceeds it by
+    // more than tau (tau = 0: on every rise); P = 2^(S c - m) <= 2^tau is
+    // quantised with the scale 448 / 2^tau
+    const float cand = fmaxf(m_run, mx);
+    const float mnew = cand > m_run + a.tau ? cand : m_run;
     const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
-    const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448;
+    const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448 + a.tau;
     m_run = mnew;
     float gs[8];
 #pragma unroll

@@ -42,6 +42,7 @@ struct AttnArgs {
   int B, H, N, n_alloc;
   int blk_q, blk_k, nblk_q, nblk_k;
   float sm_log2;          // sm_scale * log2(e)
+  float tau;              // softmax rescale threshold (log2 units, an integer)
   int n_qtiles;           // query tiles of kBM per (b, h) (dense / causal)
   // sliding-tile schedule
   const int32_t* win_off;

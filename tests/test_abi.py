@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(B):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(B.lib(), name), name
-    assert B.lib().pab_abi_version() == 1
+    assert B.lib().pab_abi_version() == 2
 
 
 def test_token_alloc_and_info(B):
@@ -104,8 +104,9 @@ def test_attention_validation_without_device(B):
     out_str = B._i64([2 * 256 * 128, 256 * 128, 128, 1])
     null = ctypes.c_void_p(0)
     f = ctypes.c_void_p(fake)
-    dense = lambda q, k, v, strides=out_str, n_out=256, sm=0.0: L.pab_attention_dense(
-        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, sm, null, null, n_out, f, strides, null)
+    dense = lambda q, k, v, strides=out_str, n_out=256, sm=0.0, tau=0: L.pab_attention_dense(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, sm, tau, null, null, n_out, f, strides,
+        null)
     assert dense(qv, kv, mk(0)) == B.PAB_INVALID_ARG          # V with the Q/K recipe
     assert dense(qv, mk(2), vv) == B.PAB_INVALID_ARG          # mixed Q/K recipes
     assert dense(qv, mk(0, n=300), vv) == B.PAB_INVALID_ARG   # shape mismatch
@@ -113,14 +114,19 @@ def test_attention_validation_without_device(B):
     assert dense(mk(0, d=96), mk(0, d=96), mk(1, d=96)) == B.PAB_UNSUPPORTED
     assert dense(qv, kv, vv, n_out=100) == B.PAB_INVALID_ARG  # output too small
     assert dense(qv, kv, vv, sm=float("nan")) == B.PAB_INVALID_ARG
+    assert dense(qv, kv, vv, tau=-1) == B.PAB_INVALID_ARG     # rescale threshold out of range
+    assert dense(qv, kv, vv, tau=9) == B.PAB_INVALID_ARG
     bad = B._i64([2 * 256 * 128, 256 * 128, 130, 1])
     assert dense(qv, kv, vv, strides=bad) == B.PAB_INVALID_ARG
-    sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, f, f, f,
+    sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, 0, f, f, f,
                               2, 100, null, null, 256, f, out_str, null)
     assert sta == B.PAB_INVALID_ARG                           # tile not a multiple of 128
-    sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, f, f, f,
+    sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, 0, f, f, f,
                               3, 128, null, null, 256, f, out_str, null)
     assert sta == B.PAB_INVALID_ARG                           # tiles do not cover N
+    sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, 12, f, f, f,
+                              2, 128, null, null, 256, f, out_str, null)
+    assert sta == B.PAB_INVALID_ARG                           # rescale threshold out of range
     assert L.pab_last_hip_error() == 0
 
 

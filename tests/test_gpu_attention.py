@@ -25,7 +25,7 @@ def _inputs(B, H, N, d, seed, dtype=torch.bfloat16, outliers=True, scale=1.0):
     return [t.float().numpy() for t in ts], ts
 
 
-def _run_dense(lib, ts, recipe, blk, causal, sm_scale=None, kv_valid=None):
+def _run_dense(lib, ts, recipe, blk, causal, sm_scale=None, kv_valid=None, tau=0):
     dev = [t.cuda() for t in ts]
     if recipe == "fp8":
         q = lib.quantize(dev[0], "fp8_block", blk)
@@ -35,12 +35,12 @@ def _run_dense(lib, ts, recipe, blk, causal, sm_scale=None, kv_valid=None):
         k = lib.quantize(dev[1], "mxfp4")
     v = lib.quantize(dev[2], "fp8_channel")
     kvv = torch.from_numpy(kv_valid).cuda() if kv_valid is not None else None
-    out = lib.attention_dense(q, k, v, causal=causal, sm_scale=sm_scale, kv_valid=kvv)
+    out = lib.attention_dense(q, k, v, causal=causal, sm_scale=sm_scale, kv_valid=kvv, tau=tau)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-def _oracle_dense(x, recipe, blk, causal, sm_scale, bn, kv_valid=None, rows=None):
+def _oracle_dense(x, recipe, blk, causal, sm_scale, bn, kv_valid=None, rows=None, tau=0):
     q, k, v = x
     B, H, N, d = q.shape
     ops = oracle_operands(q, k, v, recipe, blk)
@@ -50,7 +50,7 @@ def _oracle_dense(x, recipe, blk, causal, sm_scale, bn, kv_valid=None, rows=None
         for h in range(H):
             qo, ko, vo = ops[b][h]
             out[b, h, rows] = OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm_scale, bn=bn,
-                                                  causal=causal, kv_valid=kv_valid)
+                                                  causal=causal, kv_valid=kv_valid, tau=tau)
     return out
 
 
@@ -73,6 +73,33 @@ def test_dense_parity(gpu_lib, case):
     ref = _oracle_dense(x, case["recipe"], case["blk"], case["causal"], sm, bn)
     mx, mean = assert_close(got, ref, str(case))
     print("  max-abs %.3g mean-abs %.3g" % (mx, mean))
+
+
+@pytest.mark.parametrize("tau", [2, 8])
+@pytest.mark.parametrize("case", [
+    dict(recipe="fp8", d=128, N=1000, causal=False, blk=128),
+    dict(recipe="mxfp4", d=128, N=1000, causal=False, blk=None),
+    dict(recipe="fp8", d=128, N=700, causal=True, blk=128),
+    dict(recipe="fp8", d=64, N=520, causal=False, blk=64),
+], ids=["fp8_dense", "mxfp4_dense", "fp8_causal", "fp8_d64"])
+def test_rescale_threshold_parity(gpu_lib, case, tau):
+    """Softmax rescale threshold tau > 0 against the oracle with the same tau.
+    Key magnitudes ramp up along the sequence, so row maxima keep rising by
+    amounts on both sides of tau."""
+    print("rescale threshold", tau, case, flush=True)
+    N, d = case["N"], case["d"]
+    x, _ = _inputs(1, 2, N, d, 60 + N, torch.float32, True)
+    x[1] = x[1] * np.linspace(0.3, 3.0, N, dtype=np.float32)[None, None, :, None]
+    ts = [torch.from_numpy(a).to(torch.bfloat16) for a in x]
+    x = [t.float().numpy() for t in ts]
+    _, bn = gpu_lib.attention_info("mxfp4" if case["recipe"] == "mxfp4" else "fp8_block", d,
+                                   1 if case["causal"] else 0)
+    got = _run_dense(gpu_lib, ts, case["recipe"], case["blk"], case["causal"], tau=tau)
+    ref = _oracle_dense(x, case["recipe"], case["blk"], case["causal"], 1 / np.sqrt(d), bn, tau=tau)
+    mx, mean = assert_close(got, ref, "tau %d %s" % (tau, case))
+    print("  max-abs %.3g mean-abs %.3g" % (mx, mean))
+    eager = _run_dense(gpu_lib, ts, case["recipe"], case["blk"], case["causal"], tau=0)
+    assert not np.array_equal(got, eager), "tau had no effect"
 
 
 def test_key_padding_mask(gpu_lib):
@@ -102,25 +129,26 @@ def _sta_setup(lib, grid, real, tile, window, H=2, seed=40, outl=True):
     return hp, op, x, ts
 
 
-def _run_sta(lib, hp, ts, window_plan=None, dense=False):
+def _run_sta(lib, hp, ts, window_plan=None, dense=False, tau=0):
     dp = lib.DevicePlan(hp if window_plan is None else window_plan)
     dev = [t.cuda() for t in ts]
     q = lib.quantize(dev[0], "fp8_block", hp.tile_tokens, perm=dp.perm, n_out=dp.n_tokens)
     k = lib.quantize(dev[1], "fp8_block", hp.tile_tokens, perm=dp.perm, n_out=dp.n_tokens)
     v = lib.quantize(dev[2], "fp8_channel", perm=dp.perm, n_out=dp.n_tokens)
     if dense:
-        out = lib.attention_dense(q, k, v, kv_valid=dp.kv_valid, out_perm=dp.perm, n_out=dp.n_real)
+        out = lib.attention_dense(q, k, v, kv_valid=dp.kv_valid, out_perm=dp.perm, n_out=dp.n_real,
+                                  tau=tau)
     else:
-        out = lib.attention_sta(q, k, v, dp)
+        out = lib.attention_sta(q, k, v, dp, tau=tau)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("window", [(3, 3, 3), (1, 3, 5)])
-def test_sta_parity_with_padding(gpu_lib, window):
+@pytest.mark.parametrize("window,tau", [((3, 3, 3), 0), ((1, 3, 5), 0), ((3, 3, 3), 4)])
+def test_sta_parity_with_padding(gpu_lib, window, tau):
     grid, real, tile = (6, 16, 32), (5, 15, 30), (2, 8, 8)
     hp, op, x, ts = _sta_setup(gpu_lib, grid, real, tile, window)
-    got = _run_sta(gpu_lib, hp, ts)
+    got = _run_sta(gpu_lib, hp, ts, tau=tau)
     _, bn = gpu_lib.attention_info("fp8_block", 128, 2)
     xk = [OS.gather_tokens(a, op.perm) for a in x]
     ops = oracle_operands(*xk, "fp8", op.tile_tokens)
@@ -132,7 +160,7 @@ def test_sta_parity_with_padding(gpu_lib, window):
             rows = np.arange(u * tt, (u + 1) * tt)
             o = OA.recipe_attention(qo, ko, vo, rows, sm_scale=1 / np.sqrt(128), bn=bn,
                                     kv_valid=op.kv_valid,
-                                    key_blocks=OS.key_blocks_for_tile(op, u, bn))
+                                    key_blocks=OS.key_blocks_for_tile(op, u, bn), tau=tau)
             keep = op.perm[rows] >= 0
             ref[0, h, op.perm[rows][keep]] = o[keep]
     assert_close(got, ref, "sta %s" % (window,))
