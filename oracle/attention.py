@@ -33,12 +33,21 @@ list in ascending order; causal: keys j <= i; padded keys masked):
   O_ic = fl32(acc_c / l / rho / s_V(c)); a row with no valid key gives 0.
 (The comparison c > m + tau decides whether the reference moves; it is made
 in float32, as in the kernel.)
+
+FP4 P.V [FV §1, FP4 attention; FP4G §1, MX micro-scaling]: with V in MXFP4
+along tokens (kind 'mxfp4_tokens'), P is requantised to MXFP4 as well, per
+query row and per group of 32 consecutive keys of the tile, by the same MX
+rule as Q and K:
+    e_g   = clamp(floor(log2 max_{j in g} P_j) - 2, -127, 127)  (-127 if all 0)
+    P~_j  = E2M1(fl32(P_j 2^-e_g)) 2^e_g
+    acc_c = alpha acc_c + sum_j P~_j V^_jc, V^ = E2M1 code * 2^e_V
+    O_ic  = fl32(acc_c / l)   (the scales are inside P~ and V^)
 The products of decoded FP8 codes are exact in float64 and so are their sums
 at these lengths, so a float64 matrix product serves as the exact sum.
 """
 import numpy as np
 
-from .formats import e4m3_decode, e4m3_encode, e2m1_decode
+from .formats import e4m3_decode, e4m3_encode, e2m1_decode, e2m1_encode, f32_unbiased_exponent
 
 LOG2E = 1.4426950408889634
 
@@ -49,6 +58,8 @@ class Operand:
     kind 'fp8_block':   codes [N, d] uint8 E4M3, scales [ceil(N/blk)] float32
     kind 'mxfp4':       codes [N, d] uint8 4-bit E2M1, scales [N, d/32] uint8 E8M0
     kind 'fp8_channel': codes [N, d] uint8 E4M3, scales [d] float32
+    kind 'mxfp4_tokens' (V for FP4 P.V): codes [N, d] uint8 4-bit E2M1,
+                        scales [N/32, d] uint8 E8M0 (per channel, 32 tokens)
     """
 
     def __init__(self, kind, codes, scales, blk=None):
@@ -69,6 +80,31 @@ def _decoded(op, rows):
         vals = (vals.reshape(len(rows), d // 32, 32) * sc[..., None]).reshape(len(rows), d)
         return vals, np.ones(len(rows))
     raise ValueError(op.kind)
+
+
+def _v_decoded(v, cols):
+    """V values (float64) of the given token rows; for FP8 V without the
+    per-channel scale (the recipe divides by it at the end)."""
+    if v.kind == "mxfp4_tokens":
+        sc = np.ldexp(1.0, v.scales[cols // 32].astype(np.int64) - 127)
+        return e2m1_decode(v.codes[cols]) * sc
+    return e4m3_decode(v.codes[cols])
+
+
+def mx_requantize_p(p):
+    """MXFP4 requantisation of P (rows x keys, float32, keys in groups of 32
+    from the first column): the MX rule per row and group; returns the
+    dequantised values P~ (float64)."""
+    p = np.asarray(p, dtype=np.float32)
+    out = np.zeros(p.shape)
+    for g0 in range(0, p.shape[1], 32):
+        pg = p[:, g0:g0 + 32]
+        amax = pg.max(axis=1)
+        e = np.clip(f32_unbiased_exponent(np.where(amax > 0, amax, 1.0)) - 2, -127, 127)
+        e = np.where(amax > 0, e, -127)
+        scaled = (pg.astype(np.float64) * np.ldexp(1.0, -e)[:, None]).astype(np.float32)
+        out[:, g0:g0 + 32] = e2m1_decode(e2m1_encode(scaled)) * np.ldexp(1.0, e)[:, None]
+    return out
 
 
 def scores(q, k, qrows, kcols, sm_scale, fp64_core=False):
@@ -92,7 +128,10 @@ def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None
     """
     if int(tau) != tau or tau < 0:
         raise ValueError("tau must be a non-negative integer")
-    p_scale = 448.0 * 2.0 ** -int(tau)
+    fp4_pv = v.kind == "mxfp4_tokens"
+    if fp4_pv and bn % 32:
+        raise ValueError("FP4 P.V needs key tiles of whole 32-key groups")
+    p_scale = 1.0 if fp4_pv else 448.0 * 2.0 ** -int(tau)
     rows = np.asarray(rows, dtype=np.int64)
     n, d = k.codes.shape
     r = len(rows)
@@ -124,14 +163,19 @@ def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None
         if not fp64_core:
             p = p.astype(np.float32)
         l = alpha * l + p.astype(np.float64).sum(axis=1)
-        if quantize_p:
-            pq = e4m3_decode(e4m3_encode(np.float32(p_scale) * p.astype(np.float32)))
-        else:
+        if not quantize_p:
             pq = p_scale * p.astype(np.float64)
-        acc = alpha[:, None] * acc + pq @ e4m3_decode(v.codes[cols])
+        elif fp4_pv:
+            pq = mx_requantize_p(p)
+        else:
+            pq = e4m3_decode(e4m3_encode(np.float32(p_scale) * p.astype(np.float32)))
+        acc = alpha[:, None] * acc + pq @ _v_decoded(v, cols)
         m = m_new
     with np.errstate(invalid="ignore", divide="ignore"):
-        o = acc / l[:, None] / p_scale / v.scales.astype(np.float64)[None, :]
+        if fp4_pv:
+            o = acc / l[:, None]
+        else:
+            o = acc / l[:, None] / p_scale / v.scales.astype(np.float64)[None, :]
     o = np.where((l > 0)[:, None], o, 0.0)
     return o.astype(np.float32)
 

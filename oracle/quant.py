@@ -9,6 +9,9 @@
 [FP4G §1, micro-scaling] divide a block by a scale kept at higher precision,
            round to E2M1; dequantised value = code * scale.  The MX variant
            keeps one E8M0 (power-of-two) scale per 32 elements.
+[FV §1, FP4 attention] both products in FP4: for the P.V product V is
+           quantised to MXFP4 along the token axis (the reduction axis of
+           P.V): one E8M0 scale per channel and per 32 consecutive tokens.
 
 Readings where the pages leave a step open (listed with reasons in the design
 notes of the repository):
@@ -99,3 +102,23 @@ def mxfp4_dequantize(codes, e8m0, group=32):
     vals = e2m1_decode(codes).reshape(codes.shape[:-1] + (d // group, group))
     scale = np.ldexp(1.0, e8m0.astype(np.int64) - 127)
     return (vals * scale[..., None]).reshape(codes.shape)
+
+
+def mxfp4_token_quantize(v, group=32):
+    """MXFP4 along the token axis (second to last): one E8M0 scale per
+    channel and per `group` consecutive tokens; a last partial group counts
+    only its tokens (as zero-padded token slots would).  Returns (codes uint8
+    4-bit, same shape as v; e8m0 uint8 [..., ceil(N/group), d])."""
+    v = np.asarray(v, dtype=np.float32)
+    n = v.shape[-2]
+    npad = -(-n // group) * group
+    pad = np.zeros(v.shape[:-2] + (npad - n, v.shape[-1]), np.float32)
+    vt = np.swapaxes(np.concatenate([v, pad], axis=-2), -1, -2)
+    codes, e8 = mxfp4_quantize(vt, group)
+    return np.swapaxes(codes, -1, -2)[..., :n, :], np.swapaxes(e8, -1, -2)
+
+
+def mxfp4_token_dequantize(codes, e8m0, group=32):
+    n = codes.shape[-2]
+    sc = np.ldexp(1.0, e8m0.astype(np.int64) - 127)
+    return e2m1_decode(codes) * np.repeat(sc, group, axis=-2)[..., :n, :]

@@ -240,3 +240,49 @@ def test_lazy_rescale_tau_zero_is_the_default():
     assert np.array_equal(a, b)
     with pytest.raises(ValueError):
         A.recipe_attention(qo, ko, vo, [0], sm_scale=0.125, bn=16, tau=1.5)
+
+
+def _ops_fp4v(q, k, v):
+    qo, ko, _, qh, kh, _ = _ops(q, k, v, recipe="mxfp4")
+    vc, ve = Q.mxfp4_token_quantize(v)
+    return qo, ko, A.Operand("mxfp4_tokens", vc, ve), qh, kh, Q.mxfp4_token_dequantize(vc, ve)
+
+
+def test_fp4_p_requantisation_worked_group():
+    """The MX rule on P: group maximum 1.0 -> e = -2, P / 2^e = (4, 1.2, 0.2)
+    rounds to the E2M1 values (4, 1, 0), so P~ = (1, 0.25, 0); a group whose
+    maximum is 0.3 has e = floor(log2 0.3) - 2 = -4, 0.3 * 16 = 4.8 -> 4, P~ = 0.25."""
+    p = np.zeros((1, 64), np.float32)
+    p[0, :3] = [1.0, 0.3, 0.05]
+    p[0, 32] = 0.3
+    pq = A.mx_requantize_p(p)
+    assert np.array_equal(pq[0, :3], [1.0, 0.25, 0.0])
+    assert pq[0, 32] == 0.25 and np.count_nonzero(pq) == 3
+
+
+def test_fp4_pv_core_equals_brute_force_on_dequantised_v():
+    q, k, v = _rand(200, 128, 14, 2.0)
+    qo, ko, vo, qh, kh, vh = _ops_fp4v(q, k, v)
+    sm = 1 / np.sqrt(128)
+    o = A.recipe_attention(qo, ko, vo, np.arange(200), sm_scale=sm, bn=64, quantize_p=False,
+                           fp64_core=True)
+    assert np.allclose(o, A.brute_force(qh, kh, vh, sm), rtol=2e-7, atol=1e-7)
+
+
+def test_fp4_pv_exact_special_cases():
+    """P~ is exact when every P is 1 (equal keys: O = mean of V^ rows) and when
+    one logit dominates (P = 1 for it, the rest round to 0 within its group
+    and give empty groups elsewhere: O = that V^ row)."""
+    rng = np.random.default_rng(15)
+    n, d = 96, 128
+    q = rng.standard_normal((n, d)).astype(np.float32)
+    k = np.repeat(rng.standard_normal((1, d)).astype(np.float32), n, axis=0)
+    v = rng.standard_normal((n, d)).astype(np.float32)
+    qo, ko, vo, _, _, vh = _ops_fp4v(q, k, v)
+    o = A.recipe_attention(qo, ko, vo, np.arange(4), sm_scale=0.1, bn=64)
+    assert np.allclose(o, vh.mean(axis=0)[None, :], rtol=1e-6, atol=1e-6)
+    k2 = np.zeros((n, d), np.float32)
+    k2[50] = q[0] * 50.0                           # a logit ~ 50 sqrt(d) above the others
+    qo, ko, vo, _, _, vh = _ops_fp4v(q, k2, v)
+    o = A.recipe_attention(qo, ko, vo, [0], sm_scale=1 / np.sqrt(d), bn=64)
+    assert np.allclose(o[0], vh[50], rtol=1e-6, atol=1e-6)

@@ -137,3 +137,37 @@ def test_mxfp4_tiny_and_subnormal_groups():
     xh = Q.mxfp4_dequantize(codes, e8)
     # y = 2^-130 * 2^127 = 1/8 -> 0 ; keep sign of zero on the negative element
     assert xh[0, 0] == 0 and codes[0, 1] == 0x8
+
+
+def test_mxfp4_token_scale_belongs_to_its_channel_and_group():
+    """V for FP4 P.V: one E8M0 scale per channel and per 32 consecutive
+    tokens.  A single nonzero value at (token 37, channel 5) sets only the
+    scale of (group 1, channel 5): 3.0 -> e = floor(log2 3) - 2 = -1, code
+    3.0 / 2^-1 = 6 (E2M1 code 7)."""
+    v = np.zeros((96, 8), np.float32)
+    v[37, 5] = 3.0
+    codes, e8 = Q.mxfp4_token_quantize(v)
+    assert e8.shape == (3, 8) and codes.shape == (96, 8)
+    want = np.zeros((3, 8), np.uint8)        # all-zero groups: e = -127, code 0
+    want[1, 5] = 127 - 1
+    assert np.array_equal(e8, want)
+    assert codes[37, 5] == 7 and np.count_nonzero(codes) == 1
+    deq = Q.mxfp4_token_dequantize(codes, e8)
+    assert deq[37, 5] == 3.0 and np.count_nonzero(deq) == 1
+
+
+def test_mxfp4_token_bounds():
+    """Per (32-token group, channel): amax / 2^e in [4, 8), and every element
+    lands on the nearest E2M1 point of its group's grid after clipping at 6."""
+    rng = np.random.default_rng(12)
+    v = (rng.standard_normal((128, 16)) * np.exp(rng.standard_normal((1, 16)))).astype(np.float32)
+    codes, e8 = Q.mxfp4_token_quantize(v)
+    e = e8.astype(np.int64) - 127                               # [4, 16]
+    a = np.abs(v.astype(np.float64)).reshape(4, 32, 16)
+    ratio = a.max(axis=1) / np.ldexp(1.0, e)
+    assert np.all((ratio >= 4) & (ratio < 8))
+    y = np.minimum(a / np.ldexp(1.0, e)[:, None, :], 6.0)
+    grid = F.e2m1_decode(np.arange(8))
+    best = np.abs(y[..., None] - grid).min(-1)
+    got = np.abs(Q.mxfp4_token_dequantize(codes, e8)).reshape(4, 32, 16) / np.ldexp(1.0, e)[:, None, :]
+    assert np.array_equal(np.abs(got - y), best)
