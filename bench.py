@@ -105,9 +105,12 @@ def algorithmic_flops(cfg, plan=None):
 
 def roofline_peak(cfg):
     """Peak of the attention contraction for this recipe: MXFP4 QK^T + FP8 P.V
-    blend the FP4 and FP8 rates; the FP8 recipe is priced at the FP8 rate."""
+    blend the FP4 and FP8 rates; both products in MXFP4 run at the FP4 rate;
+    the FP8 recipe is priced at the FP8 rate."""
     if cfg.recipe == "mxfp4":
         return 2.0 / (1.0 / PEAK_FP4 + 1.0 / PEAK_FP8)
+    if cfg.recipe == "mxfp4_pv":
+        return PEAK_FP4
     return PEAK_FP8
 
 
@@ -137,7 +140,8 @@ class GpuPath:
         else:
             qq = lib.quantize(self.q, "mxfp4", None, perm, n_out)
             kq = lib.quantize(self.k, "mxfp4", None, perm, n_out)
-        vq = lib.quantize(self.v, "fp8_channel", None, perm, n_out)
+        vq = lib.quantize(self.v, "mxfp4_v" if cfg.recipe == "mxfp4_pv" else "fp8_channel", None,
+                          perm, n_out)
         return qq, kq, vq
 
     def attend(self, qq, kq, vq):
@@ -195,8 +199,12 @@ def cpu_baseline(cfg, x, plan, bn, budget_s=15.0):
         qc, qe = OQ.mxfp4_quantize(q)
         kc, ke = OQ.mxfp4_quantize(k)
         qo, ko = OA.Operand("mxfp4", qc, qe), OA.Operand("mxfp4", kc, ke)
-    vc, vs = OQ.fp8_channel_quantize(v)
-    vo = OA.Operand("fp8_channel", vc, vs)
+    if cfg.recipe == "mxfp4_pv":
+        vc, ve = OQ.mxfp4_token_quantize(v)
+        vo = OA.Operand("mxfp4_tokens", vc, ve)
+    else:
+        vc, vs = OQ.fp8_channel_quantize(v)
+        vo = OA.Operand("fp8_channel", vc, vs)
     t_quant = time.perf_counter() - t0
     sm = 1.0 / np.sqrt(cfg.d)
     n = q.shape[0]
@@ -264,7 +272,7 @@ def main():
     x = make_inputs(cfg, as_torch=True)
     path = GpuPath(cfg, x, lib, args.tau)
     mode = {"dense": 0, "causal": 1, "sta": 2}[cfg.mode]
-    _, bn = lib.attention_info("mxfp4" if cfg.recipe == "mxfp4" else "fp8_block", cfg.d, mode)
+    _, bn = lib.attention_info("fp8_block" if cfg.recipe == "fp8" else "mxfp4", cfg.d, mode)
     print("[bench] timing %d steps after %d warm-up" % (args.steps, args.warmup), file=sys.stderr,
           flush=True)
     wall, q_ms, a_ms = time_gpu(path, args.steps, args.warmup)
@@ -285,7 +293,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4+fp8" if cfg.recipe == "mxfp4" else "fp8",
+        "dtype": {"mxfp4": "mxfp4+fp8", "mxfp4_pv": "mxfp4"}.get(cfg.recipe, "fp8"),
         "data": "synthetic (seeded N(0,1), bf16, outlier channels as configured)",
         "config": {"workload": cfg.name, "desc": cfg.desc, "B": cfg.B, "H": cfg.H,
                    "N": cfg.n_real, "N_kernel": cfg.n_kernel, "d": cfg.d, "mode": cfg.mode,
@@ -297,7 +305,7 @@ def main():
                    "attention_ms_min_max": [round(min(a_ms), 4), round(max(a_ms), 4)],
                    "attention_tflops": round(achieved, 2),
                    "pct_fp8_peak": round(100 * achieved / PEAK_FP8, 2),
-                   "pct_fp4_peak": round(100 * achieved / PEAK_FP4, 2) if cfg.recipe == "mxfp4" else None},
+                   "pct_fp4_peak": round(100 * achieved / PEAK_FP4, 2) if cfg.recipe != "fp8" else None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": recorded_traffic(cfg.name) if args.tau == 0 else None},

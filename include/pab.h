@@ -68,7 +68,11 @@ typedef enum {
    * e = clamp(floor(log2 amax) - 2, -127, 127) (-127 for an all-zero group),
    * scale byte e + 127, code = E2M1(x * 2^-e), round-to-nearest-even on the
    * code, saturating at +-6; dequantised x = decode(code) * 2^e [FP4G §1]. */
-  PAB_MXFP4_D32 = 2
+  PAB_MXFP4_D32 = 2,
+  /* V for FP4 P.V [FV §1, FP4 attention]: MXFP4 along the token axis, one
+   * E8M0 scale per (batch, head, channel, 32 consecutive kernel tokens), same
+   * MX rule; zero padding slots count as tokens of their group. */
+  PAB_MXFP4_V = 3
 } pab_recipe;
 
 /* ABI version (PAB_ABI_VERSION of the built library). */
@@ -118,6 +122,14 @@ pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, in
  *  PAB_MXFP4_D32:       codes uint8 [B, H, n_alloc, d/2], two E2M1 codes per
  *                       byte, channel 2k in the low nibble;
  *                       scales uint8 (E8M0) [B, H, n_alloc, d/32].
+ *  PAB_MXFP4_V:         codes uint8 [B, H, d, n_alloc/2] - transposed, two
+ *                       E2M1 codes per byte, slot 2k in the low nibble; slot
+ *                       j of every 32-token group holds token
+ *                       8 ((j mod 16) / 4) + 4 (j / 16) + j mod 4 of the group
+ *                       (the operand order of the FP4 P.V product);
+ *                       scales uint8 (E8M0) [B, H, n_alloc/32, d] with channel
+ *                       c of a group at position 4 (c mod 32) + c / 32.
+ *                       d must be 128.
  * `operand` must be NULL for the other recipes.  x must be 16-byte aligned
  * and the batch/head/token strides multiples of 8.
  * d must be 64 or 128 (128 for MXFP4).  Inputs are assumed finite.
@@ -141,7 +153,7 @@ typedef struct {
  * pab_attention_dense - O = softmax(Q K^T * sm_scale) V, FlashAttention-style
  * [FV §2.1; FA4 FlashAttention section], on quantised operands:
  *  Q, K: PAB_FP8_TOKEN_BLOCK or PAB_MXFP4_D32 (both the same recipe);
- *  V:    PAB_FP8_CHANNEL;
+ *  V:    PAB_FP8_CHANNEL, or PAB_MXFP4_V with MXFP4 Q/K (FP4 P.V, below);
  *  P:    requantised to FP8 E4M3 with the fixed per-tensor scale 1/448
  *        [FPS §3.1]: P~ = E4M3(448 P) against the running row maximum.
  * For each query row the kernel visits key tiles of BN keys in ascending
@@ -151,6 +163,11 @@ typedef struct {
  * E4M3 values (the bf16 operand copies) with fp32 accumulation; P~ V uses the
  * FP8 matrix instructions.
  * O[i,c] = acc[i,c] / (448 l_i) / s_V[c]; a row with no valid key gives 0.
+ * FP4 P.V (V in PAB_MXFP4_V) [FV §1, FP4 attention]: P is requantised to
+ * MXFP4 instead, per query row and per 32 consecutive keys of the tile, by the
+ * MX rule of PAB_MXFP4_D32 applied to P (e = floor(log2 max P) - 2); both
+ * products run on the FP4 matrix instructions, and O = acc / l (the scales
+ * sit inside the products).  tau applies as below; there is no 448 factor.
  * sm_scale <= 0 means 1/sqrt(d)  [FV §5.2 scaling_factor].
  * tau       softmax rescale threshold, an integer in log2 units, 0 ..
  *           PAB_MAX_TAU [FA4 co-design list: conditional rescaling]: the

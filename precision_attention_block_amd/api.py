@@ -10,15 +10,17 @@ from . import binding as B
 
 
 def quantize_qkv(q, k, v, recipe="fp8", block_tokens=128, perm=None, n_out=None):
+    """recipe: "fp8" (Q/K FP8 per block), "mxfp4" (Q/K MXFP4) or "mxfp4_pv"
+    (Q/K MXFP4 and V MXFP4 along tokens: both products in FP4)."""
     if recipe == "fp8":
         qq = B.quantize(q, "fp8_block", block_tokens, perm, n_out)
         kq = B.quantize(k, "fp8_block", block_tokens, perm, n_out)
-    elif recipe == "mxfp4":
+    elif recipe in ("mxfp4", "mxfp4_pv"):
         qq = B.quantize(q, "mxfp4", None, perm, n_out)
         kq = B.quantize(k, "mxfp4", None, perm, n_out)
     else:
         raise ValueError(recipe)
-    vq = B.quantize(v, "fp8_channel", None, perm, n_out)
+    vq = B.quantize(v, "mxfp4_v" if recipe == "mxfp4_pv" else "fp8_channel", None, perm, n_out)
     return qq, kq, vq
 
 

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libpab.so")
 
 PAB_OK, PAB_INVALID_ARG, PAB_UNSUPPORTED, PAB_HIP_ERROR = 0, 1, 2, 3
 PAB_F32, PAB_BF16 = 0, 1
-RECIPES = {"fp8_block": 0, "fp8_channel": 1, "mxfp4": 2}
+RECIPES = {"fp8_block": 0, "fp8_channel": 1, "mxfp4": 2, "mxfp4_v": 3}
 TOKEN_ALIGN = 128
 
 EXPORTS = [
@@ -151,6 +151,9 @@ def quantize(x, recipe, block_tokens=None, perm=None, n_out=None, operand=True):
     elif recipe == "mxfp4":
         codes = torch.empty((B, H, na, d // 2), dtype=torch.uint8, device=dev)
         scales = torch.empty((B, H, na, d // 32), dtype=torch.uint8, device=dev)
+    elif recipe == "mxfp4_v":
+        codes = torch.empty((B, H, d, na // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, H, na // 32, d), dtype=torch.uint8, device=dev)
     else:
         raise ValueError(recipe)
     if x.dtype == torch.float32:

@@ -44,6 +44,7 @@ pab_status check_view(const pab_qview* v, int role) {
   if (v->B * v->H > (int64_t)1 << 24 || v->N > (int64_t)1 << 28) return PAB_UNSUPPORTED;
   if (!aligned(v->codes, 16)) return PAB_INVALID_ARG;
   if (role == 1) {
+    if (v->recipe == PAB_MXFP4_V) return v->d == 128 ? PAB_OK : PAB_UNSUPPORTED;
     if (v->recipe != PAB_FP8_CHANNEL) return PAB_INVALID_ARG;
     if (v->d != 64 && v->d != 128) return PAB_UNSUPPORTED;
     return PAB_OK;
@@ -67,6 +68,7 @@ pab_status fill_attn_args(const pab_qview* q, const pab_qview* k, const pab_qvie
   if ((s = check_view(k, 0)) != PAB_OK) return s;
   if ((s = check_view(v, 1)) != PAB_OK) return s;
   if (q->recipe != k->recipe) return PAB_INVALID_ARG;
+  if (v->recipe == PAB_MXFP4_V && q->recipe != PAB_MXFP4_D32) return PAB_UNSUPPORTED;
   if (q->B != k->B || q->B != v->B || q->H != k->H || q->H != v->H || q->N != k->N ||
       q->N != v->N || q->d != k->d || q->d != v->d)
     return PAB_INVALID_ARG;
@@ -97,7 +99,10 @@ pab_status fill_attn_args(const pab_qview* q, const pab_qview* k, const pab_qvie
     a.blk_q = q->block_tokens;
     a.blk_k = k->block_tokens;
   }
-  a.v_scale = static_cast<const float*>(v->scales);
+  if (v->recipe == PAB_MXFP4_V)
+    a.v_mx = static_cast<const uint8_t*>(v->scales);
+  else
+    a.v_scale = static_cast<const float*>(v->scales);
   a.kv_valid = kv_valid;
   a.out_perm = out_perm;
   a.out = out;
@@ -175,7 +180,7 @@ pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
     if (block_tokens < 16 || block_tokens > 16384 || block_tokens % 16) return PAB_INVALID_ARG;
   } else if (recipe == PAB_FP8_CHANNEL) {
     if (d != 64 && d != 128) return PAB_UNSUPPORTED;
-  } else if (recipe == PAB_MXFP4_D32) {
+  } else if (recipe == PAB_MXFP4_D32 || recipe == PAB_MXFP4_V) {
     if (d != 128) return PAB_UNSUPPORTED;
   } else {
     return PAB_INVALID_ARG;
@@ -197,7 +202,7 @@ pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
   a.n_alloc = (int)round_up(n_out, PAB_TOKEN_ALIGN);
   a.codes = static_cast<uint8_t*>(codes);
   a.values = static_cast<uint16_t*>(operand);
-  if (recipe == PAB_MXFP4_D32) {
+  if (recipe == PAB_MXFP4_D32 || recipe == PAB_MXFP4_V) {
     a.scales_u8 = static_cast<uint8_t*>(scales);
   } else {
     a.scales_f32 = static_cast<float*>(scales);
@@ -220,7 +225,7 @@ pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab
   if (s != PAB_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32,
-                                          causal ? 1 : 0, st),
+                                          v->recipe == PAB_MXFP4_V, causal ? 1 : 0, st),
                     st);
 }
 
@@ -244,7 +249,9 @@ pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_q
   a.n_tiles = n_tiles;
   a.tile_tokens = tile_tokens;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32, 2, st), st);
+  return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32,
+                                          v->recipe == PAB_MXFP4_V, 2, st),
+                    st);
 }
 
 pab_status pab_sta_plan(const int grid[3], const int real_grid[3], const int tile[3],

@@ -58,10 +58,11 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // them to 16 disjoint 4-bank groups.
 template <int CPR>
 __device__ constexpr int swz(int row) {
-  return CPR == 16 ? (row & 15) : CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+  return CPR == 16 ? (row & 15) : CPR == 8 ? ((row >> 1) & 7) : CPR == 4 ? ((row >> 2) & 3)
+                                                                          : ((row >> 3) & 1);
 }
 
-template <int D, bool MX>
+template <int D, bool MX, bool V4 = false>
 struct Tile {
   // K ring stage: FP8 recipe: K as bf16 (exact E4M3 values); MXFP4: packed
   // E2M1 plus the E8M0 group scales.
@@ -70,18 +71,24 @@ struct Tile {
   static constexpr int K_BYTES = kBN * KROW;
   static constexpr int S_BYTES = MX ? kBN * (D / 32) : 0;   // 256: one full-wave dword copy
   static constexpr int KBUF = K_BYTES + S_BYTES;
-  // V ring stage: D rows of kBN E4M3 codes of V^T
-  static constexpr int VBUF = D * kBN;
+  // V ring stage: D rows of kBN E4M3 codes of V^T; FP4 P.V (V4): D rows of
+  // kBN E2M1 codes (32 bytes) followed by the 256 E8M0 scale bytes of the tile
+  static constexpr int VROW = V4 ? kBN / 2 : kBN;
+  static constexpr int V_CPR = VROW / 16;
+  static constexpr int VCODES = D * VROW;
+  static constexpr int VSB = V4 ? 2 * D : 0;
+  static constexpr int VBUF = VCODES + VSB;
   // side ring stage: the key padding mask bytes and (FP8) the K block scales,
   // each copied as one full-wave 256-byte LDS-DMA (only the first kBN mask
   // bytes and the first few scales are used)
   static constexpr int M_BYTES = 256;
   static constexpr int ABUF = M_BYTES + (MX ? 0 : 256);
   static constexpr int KI = K_BYTES / 1024 / 4;     // LDS-DMA instructions per wave
-  static constexpr int VI = VBUF / 1024 / 4;
+  static constexpr int VI = VCODES / 1024 / 4;
   static_assert(KBUF % 16 == 0 && VBUF % 16 == 0 && ABUF % 16 == 0,
                 "LDS stages must stay 16-byte aligned");
-  static_assert(K_BYTES % 4096 == 0 && VBUF % 4096 == 0, "copy must split over 4 waves");
+  static_assert(K_BYTES % 4096 == 0 && VCODES % 4096 == 0, "copy must split over 4 waves");
+  static_assert(!V4 || (MX && D == 128), "FP4 P.V runs with MXFP4 Q/K and d = 128");
 };
 
 // Lane offsets of the LDS-DMA copy of a region of rows (16 CPR bytes each,
@@ -106,7 +113,7 @@ struct DmaPlan {
 #if defined(__HIP_DEVICE_COMPILE__)
 // (buffer descriptors and everything that uses them exist in the device pass only)
 struct HeadBuffers {
-  __amdgpu_buffer_rsrc_t k, v, s, m, c;
+  __amdgpu_buffer_rsrc_t k, v, s, m, c, vs;   // vs: E8M0 V scales (FP4 P.V)
   bool has_mask;
   int blk_k;
 };
@@ -116,10 +123,10 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw byte buffer
 // a K stage, V for a V stage plus a side stage), and every pipeline iteration
 // issues one of each, so one outstanding-copy count serves every wave and
 // iteration.
-template <int D, bool MX>
+template <int D, bool MX, bool V4 = false>
 struct Issues {
-  static constexpr int K = Tile<D, MX>::KI + (MX ? 1 : 0);
-  static constexpr int V = Tile<D, MX>::VI;
+  static constexpr int K = Tile<D, MX, V4>::KI + (MX ? 1 : 0);
+  static constexpr int V = Tile<D, MX, V4>::VI + (V4 ? 1 : 0);   // V4: plus the V scales
   static constexpr int A = MX ? 1 : 2;
 };
 
@@ -142,17 +149,37 @@ __device__ inline void issue_k(uint8_t* kbuf, const HeadBuffers& hb, int ks, int
                                              ks * (D / 32), 0, 0);
 }
 
-// Copies V^T of the key tile at `ks` into a V stage.
-template <int D, bool MX, typename VPlan>
+// V^T copy instruction `inst` of the key tile at `ks` into a V stage (rows of
+// VROW bytes, 1024 / VROW rows per instruction, n_alloc * VROW / kBN bytes
+// apart in HBM).
+template <int D, bool MX, bool V4, typename VPlan>
+__device__ inline void issue_v_inst(uint8_t* vbuf, const HeadBuffers& hb, int n_alloc, int ks,
+                                    int inst, const VPlan& vp) {
+  using TL = Tile<D, MX, V4>;
+  constexpr int RPI = 1024 / TL::VROW;
+  const int gstride = V4 ? n_alloc / 2 : n_alloc;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.v, (lds_void_t*)(vbuf + inst * 1024), 16, vp.off[0],
+                                           (V4 ? ks / 2 : ks) + inst * RPI * gstride, 0, 0);
+}
+
+// FP4 P.V: the 256 E8M0 V scale bytes of the key tile at `ks` (two 32-token
+// groups x 128 channels), one dword per lane; every wave copies the same
+// bytes to the same place.
+template <int D, bool MX, bool V4>
+__device__ inline void issue_vscale(uint8_t* vbuf, const HeadBuffers& hb, int ks, int lane) {
+  using TL = Tile<D, MX, V4>;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.vs, (lds_void_t*)(vbuf + TL::VCODES), 4, 4 * lane,
+                                           (ks / 32) * D, 0, 0);
+}
+
+// Copies V^T (and, FP4 P.V, its scales) of the key tile at `ks` into a V stage.
+template <int D, bool MX, bool V4, typename VPlan>
 __device__ inline void issue_v(uint8_t* vbuf, const HeadBuffers& hb, int n_alloc, int ks, int wave,
-                               const VPlan& vp) {
-  using TL = Tile<D, MX>;
+                               int lane, const VPlan& vp) {
+  using TL = Tile<D, MX, V4>;
 #pragma unroll
-  for (int j = 0; j < TL::VI; ++j) {
-    const int inst = wave * TL::VI + j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.v, (lds_void_t*)(vbuf + inst * 1024), 16, vp.off[0],
-                                             ks + inst * 16 * n_alloc, 0, 0);
-  }
+  for (int j = 0; j < TL::VI; ++j) issue_v_inst<D, MX, V4>(vbuf, hb, n_alloc, ks, wave * TL::VI + j, vp);
+  if (V4) issue_vscale<D, MX, V4>(vbuf, hb, ks, lane);
 }
 
 // Copies the padding mask and (FP8) the K block scales of the key tile at `ks`
@@ -219,13 +246,15 @@ __device__ inline float max3f(float a, float b, float c) { return fmaxf(fmaxf(a,
 // after it O equals the eager accumulator after tile t-1
 // (acc(t-1) = alpha(t-1) acc(t-2) + P~(t-1) V(t-1)); the last tile's rescale
 // and product follow the loop.
-template <int D, bool MX, int MODE, bool UK>
+// V4: FP4 P.V - V in MXFP4 along tokens and P requantised to MXFP4 per 32
+// keys (MXFP4 Q/K only).
+template <int D, bool MX, int MODE, bool UK, bool V4>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using TL = Tile<D, MX>;
+  using TL = Tile<D, MX, V4>;
   constexpr int DB = D / 32;            // 32-channel blocks of O^T
   constexpr int QI = D / 16;            // bf16 32x32x16 MFMAs over d (FP8 recipe)
-  constexpr int NK = Issues<D, MX>::K, NV = Issues<D, MX>::V, NA = Issues<D, MX>::A;
+  constexpr int NK = Issues<D, MX, V4>::K, NV = Issues<D, MX, V4>::V, NA = Issues<D, MX, V4>::A;
   // Distinct LDS objects per stage: the compiler can then see that a copy
   // into one stage does not alias reads of another and does not wait for it.
   __shared__ __align__(16) uint8_t k0[TL::KBUF], k1[TL::KBUF], k2[TL::KBUF];
@@ -271,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 
   const int64_t tok0 = (int64_t)bh * a.n_alloc;
   const uint8_t* kbh = (MX ? a.k : a.k16) + tok0 * TL::KROW;
-  const uint8_t* vbh = a.vt + (int64_t)bh * D * a.n_alloc;
+  const uint8_t* vbh = a.vt + (int64_t)bh * D * (V4 ? a.n_alloc / 2 : a.n_alloc);
 
   // ---- Q operand (B of S^T = K Q^T), kept in registers for the whole pass.
   // FP8: at MFMA step i lane (query lr, group lg) holds the 8 channels of
@@ -310,12 +339,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     for (int j = 0; j < 16; ++j) o[cb][j] = 0.0f;
 
   DmaPlan<TL::K_CPR> kp;
-  DmaPlan<4> vp;
+  DmaPlan<TL::V_CPR> vp;
   kp.init(lane, TL::KROW);
-  vp.init(lane, a.n_alloc);
+  vp.init(lane, V4 ? a.n_alloc / 2 : a.n_alloc);
   HeadBuffers hb;
   hb.k = __builtin_amdgcn_make_buffer_rsrc((void*)kbh, 0, a.n_alloc * TL::KROW, kRsrcWord3);
-  hb.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbh, 0, a.n_alloc * D, kRsrcWord3);
+  hb.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbh, 0, (V4 ? a.n_alloc / 2 : a.n_alloc) * D,
+                                           kRsrcWord3);
+  hb.vs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(V4 ? a.v_mx + (int64_t)bh * (a.n_alloc / 32) * D : kbh), 0,
+      V4 ? (a.n_alloc / 32) * D : 0, kRsrcWord3);
   hb.s = __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? a.k_mx + tok0 * (D / 32) : kbh), 0,
                                            MX ? a.n_alloc * (D / 32) : 0, kRsrcWord3);
   hb.has_mask = a.kv_valid != nullptr;
@@ -338,6 +371,45 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
   const int v_off0 = lr * kBN + 16 * ((2 * lg) ^ swz<4>(lr));
   const int v_off1 = lr * kBN + 16 * ((2 * lg + 1) ^ swz<4>(lr));
+  // FP4 P.V: the lane's 16-byte chunk (32 keys of group lg) of V^T row lr of
+  // a 32-channel block, and its dword of four E8M0 V scales (byte cb is the
+  // scale of channel 32 cb + lr and key group lg)
+  const int v_off4 = lr * TL::VROW + 16 * (lg ^ swz<2>(lr));
+  const int vsc_off = TL::VCODES + 128 * lg + 4 * lr;
+
+  // V^T operand of channel block cb from a V stage (FP4: only the lower four
+  // registers are set; the product below reads no more)
+  auto v_operand = [&](const uint8_t* Vs, const int cb) __attribute__((always_inline)) {
+    if (V4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(Vs + cb * 32 * TL::VROW + v_off4);
+      v8i r;
+      r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+      return r;
+    }
+    return make_v8(*reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off0),
+                   *reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off1));
+  };
+  // O^T[cb] += V^T P~^T: FP8 x FP8 with unit scales, or (FP4 P.V) E2M1 x E2M1
+  // with the V scale byte cb of vsc and the P scale ps of the lane's key group
+  auto pv_mfma = [&](const int cb, const v8i& vr, const v8i& pk, const uint32_t vsc, const int ps)
+      __attribute__((always_inline)) {
+    if (!V4) {
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vr, pk, o[cb], 0, 0, 0, 127, 0, 127);
+      return;
+    }
+    // E2M1 operands occupy four registers; the zero upper halves are never read
+    v8i a4 = {0, 0, 0, 0, 0, 0, 0, 0}, b4 = {0, 0, 0, 0, 0, 0, 0, 0};
+    a4[0] = vr[0]; a4[1] = vr[1]; a4[2] = vr[2]; a4[3] = vr[3];
+    b4[0] = pk[0]; b4[1] = pk[1]; b4[2] = pk[2]; b4[3] = pk[3];
+    if (cb == 0)
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 0, vsc, 0, ps);
+    else if (cb == 1)
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 1, vsc, 0, ps);
+    else if (cb == 2)
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 2, vsc, 0, ps);
+    else
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 3, vsc, 0, ps);
+  };
 
   // S^T (keys x queries) of the key tile in K stage `Ks`, fp32 accumulate:
   // s[kb][j] is key 32 kb + 8 (j / 4) + 4 lg + j % 4 of the tile, query myq.
@@ -369,14 +441,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // O^T += V^T P~^T (FP8 x FP8) for the tile in V stage `Vs`
-  auto pv = [&](const uint8_t* Vs, const v8i& pk) __attribute__((always_inline)) {
+  // O^T += V^T P~^T for the tile in V stage `Vs`
+  auto pv = [&](const uint8_t* Vs, const v8i& pk, const int ps) __attribute__((always_inline)) {
+    const uint32_t vsc = V4 ? *reinterpret_cast<const uint32_t*>(Vs + vsc_off) : 0u;
 #pragma unroll
-    for (int cb = 0; cb < DB; ++cb) {
-      const v8i vr = make_v8(*reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off0),
-                             *reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off1));
-      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vr, pk, o[cb], 0, 0, 0, 127, 0, 127);
-    }
+    for (int cb = 0; cb < DB; ++cb) pv_mfma(cb, v_operand(Vs, cb), pk, vsc, ps);
   };
 
   // The MFMAs of one pipeline iteration, in issue order: m < DB is the P.V
@@ -390,8 +459,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   auto read_op = [&](const int m, const uint8_t* Vs, const uint8_t* Ks, Op& op)
       __attribute__((always_inline)) {
     if (m < DB) {
-      op.a = make_v8(*reinterpret_cast<const uint4*>(Vs + m * 32 * kBN + v_off0),
-                     *reinterpret_cast<const uint4*>(Vs + m * 32 * kBN + v_off1));
+      op.a = v_operand(Vs, m);
     } else {
       const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
       const uint4 x = *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]);
@@ -399,10 +467,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       if (MX) op.sc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
     }
   };
-  auto issue_op = [&](const int m, const Op& op, v16f (&acc)[2], const v8i& pk_in)
-      __attribute__((always_inline)) {
+  auto issue_op = [&](const int m, const Op& op, v16f (&acc)[2], const v8i& pk_in,
+                      const uint32_t vsc, const int ps_in) __attribute__((always_inline)) {
     if (m < DB) {
-      o[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op.a, pk_in, o[m], 0, 0, 0, 127, 0, 127);
+      pv_mfma(m, op.a, pk_in, vsc, ps_in);
     } else {
       const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
       v16f c0;
@@ -433,7 +501,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   issue_aux<D, MX>(x0, hb, tile_at(0), lane);
   issue_k<D, MX>(k1, hb, tile_at(1), wave, lane, kp);
   issue_aux<D, MX>(x1, hb, tile_at(1), lane);
-  issue_v<D, MX>(v0, hb, a.n_alloc, tile_at(0), wave, vp);
+  issue_v<D, MX, V4>(v0, hb, a.n_alloc, tile_at(0), wave, lane, vp);
   issue_k<D, MX>(k2, hb, tile_at(2), wave, lane, kp);
 #pragma unroll
   for (int i = tid * 16; i < TL::VBUF; i += 256 * 16)
@@ -445,7 +513,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   qk(k0, sa);
   // P~ of the previous tile (read by the P.V MFMAs) and of the current one
   // alternate between pa and pb like the score buffers
-  v8i pa = {0, 0, 0, 0, 0, 0, 0, 0}, pb;
+  v8i pa = {0, 0, 0, 0, 0, 0, 0, 0}, pb = {0, 0, 0, 0, 0, 0, 0, 0};
+  int psa = 127, psb = 127;       // FP4 P.V: E8M0 scale of pa / pb for this lane's key group
   barrier_lds();                  // every wave is done with k0 before K(3) is copied there
   float alpha_prev = 1.0f;
 
@@ -453,7 +522,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // (t-1, read) and Vw (t+1, written); side stages Ar (t, read), Aw (t+2, written).
   auto iter = [&](const int t, const uint8_t* Kr, uint8_t* Kw, const uint8_t* Vr, uint8_t* Vw,
                   const uint8_t* Ar, uint8_t* Aw, v16f (&s_cur)[2], v16f (&s_nxt)[2],
-                  const v8i& pk_in, v8i& pk) __attribute__((always_inline)) {
+                  const v8i& pk_in, v8i& pk, const int ps_in, int& ps_out)
+      __attribute__((always_inline)) {
     const int ks = step_start(t);
     // this iteration's copies (K(t+3), V(t+1), side data of t+2) are issued
     // one instruction per slot below: issued back to back by every wave they
@@ -469,9 +539,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(Kw + TL::K_BYTES), 4, 4 * lane,
                                                  ks_k * (D / 32), 0, 0);
       } else if (j < NK + TL::VI) {
-        const int inst = wave * TL::VI + (j - NK);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.v, (lds_void_t*)(Vw + inst * 1024), 16, vp.off[0],
-                                                 ks_v + inst * 16 * a.n_alloc, 0, 0);
+        issue_v_inst<D, MX, V4>(Vw, hb, a.n_alloc, ks_v, wave * TL::VI + (j - NK), vp);
+      } else if (V4 && j == NK + TL::VI) {
+        issue_vscale<D, MX, V4>(Vw, hb, ks_v, lane);
       } else if (j == NK + NV) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.m, (lds_void_t*)Aw, 4, 4 * lane, ks_a, 0, 0);
       } else if (!MX && j == NK + NV + 1) {
@@ -529,15 +599,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       }
     }
 
-    // operands of the first LA slots
+    // operands of the first LA slots (and the FP4 V scales of the tile)
     Op ops[NM];
 #pragma unroll
     for (int m = 0; m < slot_lo(LA); ++m) read_op(m, Vr, Kr, ops[m]);
+    const uint32_t vsc = V4 ? *reinterpret_cast<const uint32_t*>(Vr + vsc_off) : 0u;
 
     // running max; with one factor c for the whole tile (c > 0) the max of
     // c s is c times the max of s
     float mx;
-    if (MX || UK) {
+    float gmax[2];   // FP4 P.V: maximum score of each 32-key group of the row
+    if (V4) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const v16f& x = s_cur[kb];
+        const float t0 = max3f(x[0], x[1], x[2]), t1 = max3f(x[3], x[4], x[5]);
+        const float t2 = max3f(x[6], x[7], x[8]), t3 = max3f(x[9], x[10], x[11]);
+        const float t4 = max3f(x[12], x[13], x[14]);
+        gmax[kb] = swap_max(max3f(max3f(t0, t1, t2), t3, fmaxf(t4, x[15])));
+      }
+      mx = c[0] * fmaxf(gmax[0], gmax[1]);
+    } else if (MX || UK) {
       // max3 tree over the lane's 32 scores
       float m11[11];
 #pragma unroll
@@ -561,7 +643,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
           mx = fmaxf(mx, c[4 * kb + g4] * m4);
         }
     }
-    mx = swap_max(mx);
+    if (!V4) mx = swap_max(mx);
     // the reference maximum moves only when the row maximum exceeds it by
     // more than tau (tau = 0: on every rise); P = 2^(S c - m) <= 2^tau is
     // quantised with the scale 448 / 2^tau
@@ -570,6 +652,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
     const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448 + a.tau;
     m_run = mnew;
+    // FP4 P.V: the MX rule per key group, e = floor(log2 max P) - 2 read from
+    // the exponent of 2^(c gmax - m) (-127 for an empty or subnormal group);
+    // the exponentials below then give P / 2^e in [0, 8).  c gmax is rounded
+    // as a product of its own, exactly as the row maximum above, so that the
+    // group holding the maximum gets 2^0 = 1 (a fused multiply-add would
+    // leave the product's rounding error, and 2^-tiny sets e one too low);
+    // the empty asm keeps the compiler from fusing the two.
+    int eg[2] = {0, 0};
+    float mshg[2] = {msh, msh};
+    if (V4) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float cg = c[0] * gmax[kb];
+        asm volatile("" : "+v"(cg));
+        const float pmax = gmax[kb] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(cg - mnew);
+        const int eb = (int)(__float_as_uint(pmax) >> 23);
+        eg[kb] = eb == 0 ? -127 : max(eb - 129, -127);
+        mshg[kb] = mnew == kNegInf ? 0.0f : mnew + (float)eg[kb];
+      }
+    }
 
     // The previous tile's P.V and the next tile's S are independent MFMAs;
     // they are dealt over 8 slots, one per group of 4 exponentials, and each
@@ -580,10 +682,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     float gs[8];
     v16f acc[2];
     float pq[4];   // exponentials of the previous group, packed one slot later
-    // packs group g's four P values to E4M3 and sums them; runs one slot after
-    // their exponentials so that the exp latency is hidden by other work
+    uint32_t pk4[4];   // FP4 P.V: E2M1 codes, 8 per dword, dwords 0-1 key group 0
+    // packs group g's four P values (E4M3, or E2M1 for FP4 P.V) and sums them;
+    // runs one slot after their exponentials so that the exp latency is hidden
+    // by other work
     auto finish = [&](const int g) __attribute__((always_inline)) {
       gs[g] = (pq[0] + pq[1]) + (pq[2] + pq[3]);
+      if (V4) {
+        uint32_t w;
+        if ((g & 1) == 0) {
+          asm volatile("" : "=v"(w));   // bytes 0-1 written here, 2-3 by group g + 1
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pq[0], pq[1], 1.0f, 0);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pq[2], pq[3], 1.0f, 1);
+        } else {
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk4[g / 2], pq[0], pq[1], 1.0f, 2);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pq[2], pq[3], 1.0f, 3);
+        }
+        asm volatile("" : "+v"(w), "+v"(gs[g]));
+        pk4[g / 2] = w;
+        return;
+      }
       int w;
       asm volatile("" : "=v"(w));   // the two conversions below write all four bytes
       w = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], w, false);
@@ -597,16 +715,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int m = slot_lo(g); m < slot_lo(g + 1); ++m) {
         asm volatile("" : "+v"(ops[m].a));
-        issue_op(m, ops[m], acc, pk_in);
+        issue_op(m, ops[m], acc, pk_in, vsc, ps_in);
       }
 #pragma unroll
       for (int m = slot_lo(g + LA); m < slot_lo(g + LA + 1); ++m) read_op(m, Vr, Kr, ops[m]);
       const int kb = g / 4, g4 = g % 4;
       const float cc = c[g];
+      const float sh = V4 ? mshg[kb] : msh;
       float pn[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        pn[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + j], cc, -msh));
+        pn[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + j], cc, -sh));
       if (g > 0) finish(g - 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) pq[j] = pn[j];
@@ -614,7 +733,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     finish(7);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_nxt[kb] = acc[kb];
-    const float sum = ((gs[0] + gs[1]) + (gs[2] + gs[3])) + ((gs[4] + gs[5]) + (gs[6] + gs[7]));
+    float sum;
+    if (V4) {
+      // B operand of the FP4 P.V product: lane half lg takes key group lg, its
+      // own 16 codes of that group and the other half's 16 (K slot order
+      // 8 b + r, then 8 b + 4 + r of the group, b, r < 4)
+      const auto t0 = __builtin_amdgcn_permlane32_swap(pk4[0], pk4[2], false, false);
+      const auto t1 = __builtin_amdgcn_permlane32_swap(pk4[1], pk4[3], false, false);
+      pk[0] = (int)t0[0]; pk[1] = (int)t1[0]; pk[2] = (int)t0[1]; pk[3] = (int)t1[1];
+      ps_out = 127 + (lg == 0 ? eg[0] : eg[1]);
+      sum = ldexpf((gs[0] + gs[1]) + (gs[2] + gs[3]), eg[0]) +
+            ldexpf((gs[4] + gs[5]) + (gs[6] + gs[7]), eg[1]);
+    } else {
+      sum = ((gs[0] + gs[1]) + (gs[2] + gs[3])) + ((gs[4] + gs[5]) + (gs[6] + gs[7]));
+    }
     l_run = l_run * alpha + sum;
     alpha_prev = alpha;
     // K(t+2), V(t) and the side stage of t+1 must have landed; this
@@ -625,19 +757,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // unrolled by 6: the stage rings have period 3 and the two score buffers
   // alternate, so no buffer is ever copied
   for (int t = 0; t < n_steps; t += 6) {
-    iter(t, k1, k0, v2, v1, x0, x2, sa, sb, pa, pb);
-    if (t + 1 < n_steps) iter(t + 1, k2, k1, v0, v2, x1, x0, sb, sa, pb, pa);
-    if (t + 2 < n_steps) iter(t + 2, k0, k2, v1, v0, x2, x1, sa, sb, pa, pb);
-    if (t + 3 < n_steps) iter(t + 3, k1, k0, v2, v1, x0, x2, sb, sa, pb, pa);
-    if (t + 4 < n_steps) iter(t + 4, k2, k1, v0, v2, x1, x0, sa, sb, pa, pb);
-    if (t + 5 < n_steps) iter(t + 5, k0, k2, v1, v0, x2, x1, sb, sa, pb, pa);
+    iter(t, k1, k0, v2, v1, x0, x2, sa, sb, pa, pb, psa, psb);
+    if (t + 1 < n_steps) iter(t + 1, k2, k1, v0, v2, x1, x0, sb, sa, pb, pa, psb, psa);
+    if (t + 2 < n_steps) iter(t + 2, k0, k2, v1, v0, x2, x1, sa, sb, pa, pb, psa, psb);
+    if (t + 3 < n_steps) iter(t + 3, k1, k0, v2, v1, x0, x2, sb, sa, pb, pa, psb, psa);
+    if (t + 4 < n_steps) iter(t + 4, k2, k1, v0, v2, x1, x0, sa, sb, pa, pb, psa, psb);
+    if (t + 5 < n_steps) iter(t + 5, k0, k2, v1, v0, x2, x1, sb, sa, pb, pa, psb, psa);
   }
   // the last tile's product: V(n_steps - 1) sits in stage (n_steps - 1) % 3
   {
 #pragma unroll
     for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha_prev;
     const int r = (n_steps - 1) % 3;
-    pv(r == 0 ? v0 : r == 1 ? v1 : v2, (n_steps & 1) ? pb : pa);
+    pv(r == 0 ? v0 : r == 1 ? v1 : v2, (n_steps & 1) ? pb : pa, (n_steps & 1) ? psb : psa);
     // keep these MFMAs here, with every lane active: sunk into the store
     // branch below they would run on a partial EXEC mask, which drops the
     // operand rows of the inactive lanes
@@ -646,7 +778,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
   wait_vm_le<0>();   // no copy may still target this workgroup's LDS when it ends
 
-  // ---- epilogue: O = acc / (448 l) / s_V, stored through the output permutation
+  // ---- epilogue: O = acc / (448 l) / s_V (FP4 P.V: acc / l), stored through
+  // the output permutation
   const float lt = swap_sum(l_run);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (myq < a.N) {
@@ -654,17 +787,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     if (tok >= 0) {
       const int b = bh / a.H, h = bh % a.H;
       float* orow = a.out + b * a.osb + h * a.osh + (int64_t)tok * a.osn;
-      const float* vs = a.v_scale + (int64_t)bh * D;
+      const float* vs = V4 ? nullptr : a.v_scale + (int64_t)bh * D;
 #pragma unroll
       for (int cb = 0; cb < DB; ++cb)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int c0 = 32 * cb + 8 * g4 + 4 * lg;
           float4 r;
-          r.x = o[cb][4 * g4 + 0] * inv / vs[c0 + 0];
-          r.y = o[cb][4 * g4 + 1] * inv / vs[c0 + 1];
-          r.z = o[cb][4 * g4 + 2] * inv / vs[c0 + 2];
-          r.w = o[cb][4 * g4 + 3] * inv / vs[c0 + 3];
+          if (V4) {
+            r.x = o[cb][4 * g4 + 0] * inv;
+            r.y = o[cb][4 * g4 + 1] * inv;
+            r.z = o[cb][4 * g4 + 2] * inv;
+            r.w = o[cb][4 * g4 + 3] * inv;
+          } else {
+            r.x = o[cb][4 * g4 + 0] * inv / vs[c0 + 0];
+            r.y = o[cb][4 * g4 + 1] * inv / vs[c0 + 1];
+            r.z = o[cb][4 * g4 + 2] * inv / vs[c0 + 2];
+            r.w = o[cb][4 * g4 + 3] * inv / vs[c0 + 3];
+          }
           *reinterpret_cast<float4*>(orow + c0) = r;
         }
     }
@@ -1129,23 +1269,25 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool MX, int MODE>
+template <int D, bool MX, int MODE, bool V4>
 static hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const bool uk = MX || a.blk_k % kBN == 0;
   const int64_t blocks = MODE == 2 ? (int64_t)a.B * a.H * a.n_tiles * (a.tile_tokens / kBM)
                                    : (int64_t)a.B * a.H * a.n_qtiles;
   if (uk)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, MX, MODE, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, MX, MODE, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, MX, MODE, true, V4>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       a);
+  else if constexpr (!MX)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, MX, MODE, false, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       st, a);
   return hipGetLastError();
 }
 
-template <int D, bool MX>
+template <int D, bool MX, bool V4 = false>
 static hipError_t launch_mode(const AttnArgs& a, int mode, hipStream_t st) {
-  if (mode == 1) return launch_t<D, MX, 1>(a, st);
-  if (mode == 2) return launch_t<D, MX, 2>(a, st);
-  return launch_t<D, MX, 0>(a, st);
+  if (mode == 1) return launch_t<D, MX, 1, V4>(a, st);
+  if (mode == 2) return launch_t<D, MX, 2, V4>(a, st);
+  return launch_t<D, MX, 0, V4>(a, st);
 }
 
 template <bool MX, int MODE>
@@ -1159,10 +1301,11 @@ static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, int d, bool mx, int mode, hipStream_t st) {
+hipError_t launch_attention(const AttnArgs& a, int d, bool mx, bool v4, int mode, hipStream_t st) {
   // dense FP8 with d = 128: the ping-pong kernel (its matrix phase, with QK^T
   // on the bf16 MFMA, is long enough to balance the vector phase; for MXFP4
   // and for causal masks the 4-wave kernel measures faster)
+  if (v4) return mx && d == 128 ? launch_mode<128, true, true>(a, mode, st) : hipErrorInvalidValue;
   if (!mx && d == 128 && mode == 0) return launch_pp<false, 0>(a, st);
   if (mx) return launch_mode<128, true>(a, mode, st);
   if (d == 64) return launch_mode<64, false>(a, mode, st);

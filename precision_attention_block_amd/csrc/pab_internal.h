@@ -12,7 +12,7 @@ struct QuantArgs {
   const void* x;          // input base pointer
   int64_t sb, sh, sn;     // element strides of batch, head, token (channel stride 1)
   int B, H, N_in, d;
-  int recipe;             // 0 FP8 per block, 1 FP8 per channel, 2 MXFP4
+  int recipe;             // 0 FP8 per block, 1 FP8 per channel, 2 MXFP4, 3 MXFP4 V (tokens)
   bool in_bf16;
   int blk, nblk;          // FP8 per block: tokens per block, blocks per (b, h)
   const int32_t* perm;    // nullable token gather
@@ -20,7 +20,7 @@ struct QuantArgs {
   uint8_t* codes;
   uint16_t* values;       // FP8 per block: bf16 copy of each code's exact value (nullable)
   float* scales_f32;      // FP8 recipes
-  uint8_t* scales_u8;     // MXFP4
+  uint8_t* scales_u8;     // MXFP4 recipes
 };
 
 // Arguments of the attention kernel.
@@ -29,7 +29,9 @@ struct AttnArgs {
   const uint8_t* k;
   const uint8_t* q16;     // FP8 recipe: bf16 values of the E4M3 codes [BH][n_alloc][d]
   const uint8_t* k16;
-  const uint8_t* vt;      // FP8 V^T [BH][d][n_alloc], operand-ordered per 64 tokens
+  const uint8_t* vt;      // FP8 V^T [BH][d][n_alloc], operand-ordered per 64 tokens;
+                          // FP4 P.V: MXFP4 V^T [BH][d][n_alloc/2]
+  const uint8_t* v_mx;    // FP4 P.V: E8M0 V scales [BH][n_alloc/32][d] (channels interleaved)
   const float* q_scale;   // FP8: [BH][nblk_q]
   const float* k_scale;   // FP8: [BH][nblk_k]
   const uint8_t* q_mx;    // MXFP4: [BH][n_alloc][d/32]
@@ -57,6 +59,7 @@ constexpr int kBN = 64;       // keys per online-softmax step
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
 hipError_t launch_count_nonfinite(const float* x, int64_t n, int32_t* count, hipStream_t st);
 // mode: 0 dense, 1 causal, 2 sliding-tile
-hipError_t launch_attention(const AttnArgs& a, int d, bool mx, int mode, hipStream_t st);
+// v4: V in MXFP4 along tokens (FP4 P.V; MXFP4 Q/K, d = 128)
+hipError_t launch_attention(const AttnArgs& a, int d, bool mx, bool v4, int mode, hipStream_t st);
 
 }  // namespace pab

@@ -8,6 +8,10 @@
 //    order of the attention kernel's P.V product, then a pass that turns the
 //    amax into the scale.
 //  * Q/K MXFP4 [FP4G §1]: one thread per 32-channel group.
+//  * V MXFP4 along tokens (FP4 P.V, [FV §1] FP4 attention): a 64-token tile
+//    of one head is transposed through LDS; one thread per (channel, group of
+//    32 tokens) derives the E8M0 scale and writes the 32 codes in the operand
+//    order of the attention kernel's FP4 P.V product.
 // Optional token gather (perm) implements the block transpose of [FPS §3.3
 // item 1]: kernel token p reads input token perm[p]; -1 yields a zero token.
 //
@@ -276,6 +280,60 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(QuantArgs a) {
   }
 }
 
+// ------------------------------------------------------------ MXFP4 V (tokens)
+// Token slot j (0..31) of a 32-token group holds token pi(j): the K order of
+// the FP4 P.V product, whose lanes hold keys 8b + r (first 16 slots) and
+// 8b + 4 + r (last 16) of the group, b and r < 4.
+__device__ constexpr int v4_token_of_slot(int j) { return 8 * ((j % 16) / 4) + 4 * (j / 16) + j % 4; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void quant_mxfp4_v_kernel(QuantArgs a) {
+  constexpr int D = 128, TT = 64, LD = TT + 1;   // LDS row: one channel, 64 tokens (+1 pad)
+  __shared__ float tile[D * LD];
+  const int bh = blockIdx.y, t0 = blockIdx.x * TT, tid = threadIdx.x;
+  // load: unit = (token, 8-channel chunk), 64 x 16 units
+  for (int u = tid; u < TT * (D / 8); u += 256) {
+    const int t = u / (D / 8), ch = u % (D / 8);
+    float w[8];
+    const int src = src_token(a, t0 + t);
+    if (src >= 0) {
+      load8(token_ptr<T>(a, bh, src) + 8 * ch, w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[(8 * ch + j) * LD + t] = w[j];
+  }
+  __syncthreads();
+  const int c = tid % D, g = tid / D;            // channel, 32-token group of the tile
+  const float* row = tile + c * LD + 32 * g;
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(row[j]));
+  // the MX rule as for Q/K: e = floor(log2 amax) - 2 from the exponent field,
+  // -127 for a zero or subnormal amax
+  const int e32 = (int)(__float_as_uint(amax) >> 23);
+  const int e = e32 == 0 ? -127 : max(e32 - 127 - 2, -127);
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(row[v4_token_of_slot(8 * q + i)], inv);
+    uint32_t p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, y[2], y[3], 1.0f, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, y[4], y[5], 1.0f, 2);
+    w[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, y[6], y[7], 1.0f, 3);
+  }
+  uint8_t* out = a.codes + ((int64_t)bh * D + c) * (a.n_alloc / 2) + (t0 + 32 * g) / 2;
+  *reinterpret_cast<uint4*>(out) = make_uint4(w[0], w[1], w[2], w[3]);
+  // scales [group][channel], channels interleaved: c at 4 (c % 32) + c / 32
+  a.scales_u8[((int64_t)bh * (a.n_alloc / 32) + t0 / 32 + g) * D + 4 * (c % 32) + c / 32] =
+      (uint8_t)(e + 127);
+}
+
 // ------------------------------------------------------------ non-finite count
 __global__ void count_nonfinite_kernel(const float* x, int64_t n, int32_t* count) {
   int c = 0;
@@ -317,10 +375,18 @@ static hipError_t launch_mxfp4(const QuantArgs& a, hipStream_t st) {
 }
 
 template <typename T>
+static hipError_t launch_mxfp4_v(const QuantArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.n_alloc / 64), (unsigned)(a.B * a.H));   // n_alloc % 128 == 0
+  hipLaunchKernelGGL((quant_mxfp4_v_kernel<T>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T>
 static hipError_t dispatch_quant(const QuantArgs& a, hipStream_t st) {
   switch (a.recipe) {
     case 0: return a.d == 128 ? launch_fp8_block<T, 128>(a, st) : launch_fp8_block<T, 64>(a, st);
     case 1: return a.d == 128 ? launch_channel<T, 128>(a, st) : launch_channel<T, 64>(a, st);
+    case 3: return launch_mxfp4_v<T>(a, st);
     default: return launch_mxfp4<T>(a, st);
   }
 }

@@ -69,8 +69,12 @@ def head_job(job):
         qc, qs = OQ.mxfp4_quantize(q)
         kc, ks = OQ.mxfp4_quantize(k)
         qo, ko = OA.Operand("mxfp4", qc, qs), OA.Operand("mxfp4", kc, ks)
-    vc, vs = OQ.fp8_channel_quantize(v)
-    vo = OA.Operand("fp8_channel", vc, vs)
+    if cfg.recipe == "mxfp4_pv":
+        vc, vs = OQ.mxfp4_token_quantize(v)
+        vo = OA.Operand("mxfp4_tokens", vc, vs)
+    else:
+        vc, vs = OQ.fp8_channel_quantize(v)
+        vo = OA.Operand("fp8_channel", vc, vs)
     digests = {"q": digest(qc, qs), "k": digest(kc, ks), "v": digest(vc, vs)}
     sm = 1.0 / np.sqrt(cfg.d)
     out = np.zeros((len(rows), cfg.d), np.float32)

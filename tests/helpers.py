@@ -46,8 +46,13 @@ def oracle_operands(q, k, v, recipe, blk):
                 qc, qe = OQ.mxfp4_quantize(q[b, h])
                 kc, ke = OQ.mxfp4_quantize(k[b, h])
                 qo, ko = OA.Operand("mxfp4", qc, qe), OA.Operand("mxfp4", kc, ke)
-            vc, vs = OQ.fp8_channel_quantize(v[b, h])
-            out[b][h] = (qo, ko, OA.Operand("fp8_channel", vc, vs))
+            if recipe == "mxfp4_pv":
+                vc, ve = OQ.mxfp4_token_quantize(v[b, h])
+                vo = OA.Operand("mxfp4_tokens", vc, ve)
+            else:
+                vc, vs = OQ.fp8_channel_quantize(v[b, h])
+                vo = OA.Operand("fp8_channel", vc, vs)
+            out[b][h] = (qo, ko, vo)
     return out
 
 
@@ -83,3 +88,28 @@ def oracle_sta(x, grid, real_grid, tile, window, blk, bn, sm_scale):
                 keep = op.perm[rows] >= 0
                 ref[b, h, op.perm[rows][keep]] = o[keep]
     return ref
+
+
+V4_SLOT_TOKEN = np.array([8 * ((j % 16) // 4) + 4 * (j // 16) + j % 4 for j in range(32)])
+
+
+def v4_codes_to_tokens(codes_t, n):
+    """GPU MXFP4 V codes [d, n_alloc/2] (two per byte, low nibble first, slot j
+    of every 32-token group holding token V4_SLOT_TOKEN[j]) -> [n, d] codes in
+    token order."""
+    b = np.asarray(codes_t)
+    d = b.shape[0]
+    nib = np.empty((d, b.shape[1] * 2), np.uint8)
+    nib[:, 0::2] = b & 0xF
+    nib[:, 1::2] = b >> 4
+    g = nib.reshape(d, -1, 32)
+    tok = np.empty_like(g)
+    tok[:, :, V4_SLOT_TOKEN] = g
+    return tok.reshape(d, -1)[:, :n].T
+
+
+def v4_scales_to_channels(scales, d=128):
+    """GPU MXFP4 V scales [n_alloc/32, d] (channel c at 4 (c % 32) + c / 32)
+    -> [n_alloc/32, d] in channel order."""
+    c = np.arange(d)
+    return np.asarray(scales)[:, 4 * (c % 32) + c // 32]

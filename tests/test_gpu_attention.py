@@ -209,3 +209,63 @@ def test_nonfinite_count(gpu_lib):
     x = torch.zeros(1000, device="cuda")
     x[[3, 500, 999]] = torch.tensor([float("nan"), float("inf"), -float("inf")], device="cuda")
     assert int(gpu_lib.count_nonfinite(x).item()) == 3
+
+
+def _run_fp4pv(lib, ts, causal=False, tau=0, plan=None):
+    dev = [t.cuda() for t in ts]
+    perm = plan.perm if plan is not None else None
+    n_out = plan.n_tokens if plan is not None else None
+    q = lib.quantize(dev[0], "mxfp4", None, perm, n_out)
+    k = lib.quantize(dev[1], "mxfp4", None, perm, n_out)
+    v = lib.quantize(dev[2], "mxfp4_v", None, perm, n_out)
+    if plan is not None:
+        out = lib.attention_sta(q, k, v, plan, tau=tau)
+    else:
+        out = lib.attention_dense(q, k, v, causal=causal, tau=tau)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", [
+    dict(N=1000, causal=False, tau=0),
+    dict(N=700, causal=True, tau=0),
+    dict(N=520, causal=False, tau=4),
+], ids=["dense", "causal", "tau4"])
+def test_fp4_pv_parity(gpu_lib, case):
+    """FP4 P.V (MXFP4 Q/K, V in MXFP4 along tokens, P requantised per 32 keys)
+    against the oracle recipe, every output element."""
+    print("fp4 p.v", case, flush=True)
+    N = case["N"]
+    x, ts = _inputs(1, 2, N, 128, 80 + N, torch.bfloat16, True)
+    got = _run_fp4pv(gpu_lib, ts, case["causal"], case["tau"])
+    _, bn = gpu_lib.attention_info("mxfp4", 128, 1 if case["causal"] else 0)
+    ops = oracle_operands(*x, "mxfp4_pv", None)
+    ref = np.zeros_like(got)
+    for h in range(2):
+        qo, ko, vo = ops[0][h]
+        ref[0, h] = OA.recipe_attention(qo, ko, vo, np.arange(N), sm_scale=1 / np.sqrt(128), bn=bn,
+                                        causal=case["causal"], tau=case["tau"])
+    mx, mean = assert_close(got, ref, "fp4 p.v %s" % case)
+    print("  max-abs %.3g mean-abs %.3g" % (mx, mean))
+
+
+def test_fp4_pv_sta(gpu_lib):
+    grid, real, tile, window = (6, 16, 32), (5, 15, 30), (2, 8, 8), (3, 3, 3)
+    hp, op, x, ts = _sta_setup(gpu_lib, grid, real, tile, window, seed=44)
+    dp = gpu_lib.DevicePlan(hp)
+    got = _run_fp4pv(gpu_lib, ts, plan=dp)
+    _, bn = gpu_lib.attention_info("mxfp4", 128, 2)
+    xk = [OS.gather_tokens(a, op.perm) for a in x]
+    ops = oracle_operands(*xk, "mxfp4_pv", None)
+    ref = np.zeros_like(got)
+    tt = op.tile_tokens
+    for h in range(2):
+        qo, ko, vo = ops[0][h]
+        for u in range(op.n_tiles):
+            rows = np.arange(u * tt, (u + 1) * tt)
+            o = OA.recipe_attention(qo, ko, vo, rows, sm_scale=1 / np.sqrt(128), bn=bn,
+                                    kv_valid=op.kv_valid, key_blocks=OS.key_blocks_for_tile(op, u, bn))
+            keep = op.perm[rows] >= 0
+            ref[0, h, op.perm[rows][keep]] = o[keep]
+    mx, mean = assert_close(got, ref, "fp4 p.v sta")
+    print("  max-abs %.3g mean-abs %.3g" % (mx, mean))

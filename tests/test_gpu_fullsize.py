@@ -13,7 +13,8 @@ import torch
 
 from oracle import formats as OF
 from tests import fullsize as FS
-from tests.helpers import MAX_ABS, MEAN_ABS, vt_to_tokens
+from tests.helpers import (MAX_ABS, MEAN_ABS, v4_codes_to_tokens, v4_scales_to_channels,
+                           vt_to_tokens)
 from workloads import CONFIGS, make_inputs, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -39,7 +40,7 @@ def _gpu_run(lib, cfg, x):
     else:
         qq = lib.quantize(q, "mxfp4", None, perm, n_out)
         kq = lib.quantize(k, "mxfp4", None, perm, n_out)
-    vq = lib.quantize(v, "fp8_channel", None, perm, n_out)
+    vq = lib.quantize(v, "mxfp4_v" if cfg.recipe == "mxfp4_pv" else "fp8_channel", None, perm, n_out)
     del q, k, v
     if cfg.mode == "sta":
         out = lib.attention_sta(qq, kq, vq, dplan)
@@ -63,19 +64,24 @@ def _gpu_digests(cfg, qq, kq, vq, head):
         else:
             out[name] = FS.digest(OF.e2m1_unpack(codes), t.scales[0, head].cpu().numpy()[:n])
     vt = vq.codes[0, head].cpu().numpy()
-    out["v"] = FS.digest(vt_to_tokens(vt, n), vq.scales[0, head].cpu().numpy())
+    if cfg.recipe == "mxfp4_pv":
+        sc = v4_scales_to_channels(vq.scales[0, head].cpu().numpy())
+        out["v"] = FS.digest(v4_codes_to_tokens(vt, n), sc[:-(-n // 32)])
+    else:
+        out["v"] = FS.digest(vt_to_tokens(vt, n), vq.scales[0, head].cpu().numpy())
     return out
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["llm_prefill_fp8_causal", "dense_mxfp4_16k", "dense_fp8_16k",
-                                  "sta_46k_fp8", "video_92k_fp8_dense", "video_92k_fp8_sta"])
+@pytest.mark.parametrize("name", ["llm_prefill_fp8_causal", "dense_mxfp4_16k", "dense_mxfp4_pv_16k",
+                                  "dense_fp8_16k", "sta_46k_fp8", "video_92k_fp8_dense",
+                                  "video_92k_fp8_sta"])
 def test_full_size_sampled_rows(gpu_lib, name):
     cfg = CONFIGS[name]
     print("full size", name, "rows", ROWS, "workers", WORKERS, flush=True)
     x = make_inputs(cfg, as_torch=True)
     mode = {"dense": 0, "causal": 1, "sta": 2}[cfg.mode]
-    _, bn = gpu_lib.attention_info("mxfp4" if cfg.recipe == "mxfp4" else "fp8_block", cfg.d, mode)
+    _, bn = gpu_lib.attention_info("fp8_block" if cfg.recipe == "fp8" else "mxfp4", cfg.d, mode)
     heads, tokens = sample_rows(cfg, ROWS)
     shms = []
     try:

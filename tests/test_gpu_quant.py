@@ -156,3 +156,29 @@ def test_fp8_conversion_exhaustive_binades(gpu_lib, lo, hi):
         bad = np.nonzero(got != want)[0]
         assert len(bad) == 0, "first mismatch: x=%r got %02x want %02x" % (
             x.reshape(-1)[bad[0]], got[bad[0]], want[bad[0]])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("N", [256, 300, 1000])
+def test_mxfp4_v_bit_exact(gpu_lib, dtype, N):
+    """V in MXFP4 along tokens (FP4 P.V): codes and E8M0 scales equal the
+    oracle's bit for bit after undoing the documented layout (transposed, slot
+    order of the FP4 P.V operand, interleaved channels); padding slots are
+    zero codes."""
+    from tests.helpers import v4_codes_to_tokens, v4_scales_to_channels
+    x, t = _inputs((1, 2, N, 128), 70 + N, dtype, True)
+    x[0, 1, 5:9] *= 1000.0                       # a group with a large exponent
+    t = torch.from_numpy(x).to(dtype)
+    x = t.float().numpy()
+    qt = gpu_lib.quantize(t.cuda(), "mxfp4_v")
+    na = gpu_lib.token_alloc(N)
+    codes = qt.codes.cpu().numpy()
+    scales = qt.scales.cpu().numpy()
+    assert codes.shape == (1, 2, 128, na // 2) and scales.shape == (1, 2, na // 32, 128)
+    for h in range(2):
+        rc, re = OQ.mxfp4_token_quantize(x[0, h])
+        got = v4_codes_to_tokens(codes[0, h], na)
+        assert np.array_equal(got[:N], rc), "codes differ, head %d" % h
+        assert not got[N:].any(), "padding codes not zero"
+        gs = v4_scales_to_channels(scales[0, h])
+        assert np.array_equal(gs[:re.shape[0]], re), "scales differ, head %d" % h

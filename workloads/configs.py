@@ -4,6 +4,8 @@ latents of a 720p Wan2.1-class model (FPSAttention page, §1 and §2.2).
 
 recipe  'fp8'   : Q/K FP8 E4M3 per `blk`-token block, V FP8 per channel
         'mxfp4' : Q/K E2M1 with one E8M0 scale per 32 channels, V FP8 per channel
+        'mxfp4_pv': Q/K as 'mxfp4', V MXFP4 along tokens and P requantised to
+                  MXFP4 per 32 keys (both products in FP4)
 mode    'dense' | 'causal' | 'sta'
 grid    (T, H, W) of the zero-padded latent grid, real_grid the unpadded one;
         tokens are given in raster order over real_grid.
@@ -60,6 +62,10 @@ CONFIGS = {
         "dense_mxfp4_16k", 3, B=1, H=40, d=128, recipe="mxfp4", blk=32,
         mode="dense", dtype="bf16", outliers=True, N=16384,
         desc="dense MXFP4 Q/K: B1 H40 N16384 d128, bf16 + outliers, FP8 V"),
+    "dense_mxfp4_pv_16k": Config(
+        "dense_mxfp4_pv_16k", 3, B=1, H=40, d=128, recipe="mxfp4_pv", blk=32,
+        mode="dense", dtype="bf16", outliers=True, N=16384,
+        desc="dense FP4 attention: the 16K MXFP4 shape (same inputs) with V and P in MXFP4 too"),
     "dense_fp8_16k": Config(
         "dense_fp8_16k", 3, B=1, H=40, d=128, recipe="fp8", blk=128,
         mode="dense", dtype="bf16", outliers=True, N=16384,
