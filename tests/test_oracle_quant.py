@@ -171,3 +171,17 @@ def test_mxfp4_token_bounds():
     best = np.abs(y[..., None] - grid).min(-1)
     got = np.abs(Q.mxfp4_token_dequantize(codes, e8)).reshape(4, 32, 16) / np.ldexp(1.0, e)[:, None, :]
     assert np.array_equal(np.abs(got - y), best)
+
+
+def test_mxfp4_token_partial_group():
+    """N = 40 tokens: the second group holds tokens 32..39 only, and its scale
+    comes from them alone (amax 0.75 -> e = floor(log2 0.75) - 2 = -3)."""
+    v = np.zeros((40, 2), np.float32)
+    v[:32, 0] = 4.0                       # group 0: e = 0
+    v[35, 0] = 0.75
+    v[39, 1] = -0.5                       # group 1, channel 1: e = -3, code -4 (0xE)
+    codes, e8 = Q.mxfp4_token_quantize(v)
+    assert e8.shape == (2, 2) and codes.shape == (40, 2)
+    assert e8[0, 0] == 127 and e8[1, 0] == 127 - 3 and e8[1, 1] == 127 - 3
+    deq = Q.mxfp4_token_dequantize(codes, e8)
+    assert deq[35, 0] == 0.75 and deq[39, 1] == -0.5 and np.all(deq[:32, 0] == 4.0)
