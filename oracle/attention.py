@@ -117,8 +117,12 @@ def scores(q, k, qrows, kcols, sm_scale, fp64_core=False):
 
 
 def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None,
-                     key_blocks=None, quantize_p=True, fp64_core=False, tau=0):
+                     key_blocks=None, quantize_p=True, fp64_core=False, tau=0, return_lse=False):
     """Output rows O[rows, :] (float32) of one (batch, head).
+
+    return_lse: also return the row statistic LSE_i = m_i + log2(l_i)
+    (float32, log2 units of S; -inf for a row without a valid key), which
+    gives the softmax row as P_ij = 2^(S_ij - LSE_i) for the backward pass.
 
     key_blocks: None (all BN-key tiles 0..ceil(N/BN)-1) or an ascending list of
     key-tile start indices shared by every row in `rows`.
@@ -177,6 +181,10 @@ def recipe_attention(q, k, v, rows, *, sm_scale, bn, causal=False, kv_valid=None
         else:
             o = acc / l[:, None] / p_scale / v.scales.astype(np.float64)[None, :]
     o = np.where((l > 0)[:, None], o, 0.0)
+    if return_lse:
+        with np.errstate(divide="ignore", invalid="ignore"):
+            lse = np.where(l > 0, m.astype(np.float64) + np.log2(l), -np.inf)
+        return o.astype(np.float32), lse.astype(np.float32)
     return o.astype(np.float32)
 
 
