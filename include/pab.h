@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define PAB_ABI_VERSION 2
+#define PAB_ABI_VERSION 3
 #define PAB_TOKEN_ALIGN 128  /* query tile of the attention kernel */
 #define PAB_MAX_TAU 8        /* largest softmax rescale threshold (log2 units) */
 
@@ -184,11 +184,16 @@ typedef struct {
  * out       device float32 [B, H, n_out_tokens, d] with element strides
  *           out_strides (innermost 1); rows that no query maps to are not
  *           written.
+ * lse       device float32 [B, H, N] or NULL: the row statistic
+ *           LSE_i = m_i + log2(sum_j 2^(S_ij - m_i)) in the log2 units of S
+ *           (S = Q K^T * sm_scale * log2(e)), stored per query in the kernel's
+ *           token order whatever out_perm is; -inf for a row without a valid
+ *           key.  The backward pass recovers P from it.
  */
 pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab_qview* v,
                                int causal, float sm_scale, int tau, const uint8_t* kv_valid,
                                const int32_t* out_perm, int64_t n_out_tokens, float* out,
-                               const int64_t out_strides[4], void* stream);
+                               const int64_t out_strides[4], float* lse, void* stream);
 
 /*
  * pab_attention_sta - sliding-tile sparse attention [FPS §2.2]: the N tokens
@@ -201,14 +206,53 @@ pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab
  * int32 [n_tiles] (a permutation of the tiles: the order work is issued, e.g.
  * longest window first [FA4, LPT scheduling]) - device pointers.
  * tile_tokens must be a multiple of PAB_TOKEN_ALIGN and N == n_tiles *
- * tile_tokens.
+ * tile_tokens.  lse as in pab_attention_dense.
  */
 pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_qview* v,
                              float sm_scale, int tau, const int32_t* win_off, const int32_t* win_idx,
                              const int32_t* tile_order, int n_tiles, int tile_tokens,
                              const uint8_t* kv_valid, const int32_t* out_perm,
                              int64_t n_out_tokens, float* out, const int64_t out_strides[4],
-                             void* stream);
+                             float* lse, void* stream);
+
+/*
+ * pab_attention_backward - gradients of the attention of pab_attention_dense
+ * [FA4 co-design list: the backward pass, intermediates S, P, dP, dS, dQ],
+ * for training-aware quantisation [FPS introduction].  The quantisers pass
+ * gradients straight through: the results are the gradients with respect to
+ * the dequantised operands Q^, K^, V^ of
+ *     O = softmax(Q^ K^T * sm_scale) V^,
+ * evaluated with the forward's row statistic and output:
+ *     P = 2^(S - LSE) with S = Q^ K^T * sm_scale * log2(e)
+ *     dV = P^T dO,  dP = dO V^^T,  D_i = sum_c dO_ic O_ic,
+ *     dS = P (dP - D),  dQ = sm_scale dS K^,  dK = sm_scale dS^T Q^.
+ * q, k, v   the views the forward pass used: Q/K PAB_FP8_TOKEN_BLOCK (with its
+ *           operand copy) or PAB_MXFP4_D32; V PAB_FP8_CHANNEL or PAB_MXFP4_V;
+ *           d = 128.
+ * causal, sm_scale, kv_valid   as passed to the forward (sm_scale <= 0 means
+ *           1/sqrt(d)).
+ * out       the forward output O, float32 [B, H, N, d] in the kernel's token
+ *           order (the forward called without out_perm), strides out_strides.
+ * dout      dO, float32 or bf16 (dout_dtype) [B, H, N, d], strides
+ *           dout_strides (innermost 1).
+ * lse       the forward's lse, float32 [B, H, N].
+ * dq, dk, dv  float32 [B, H, N, d] with strides grad_strides (innermost 1);
+ *           every element of rows 0..N-1 is written.
+ * workspace device memory of at least
+ *           pab_attention_backward_workspace(B, H, N, d) bytes, 256-byte
+ *           aligned, owned by the caller; contents on entry do not matter.
+ * P, dS and dO enter their matrix products rounded to bf16; sums are fp32.
+ * Strides must be multiples of 4 (float32) or 8 (bf16) elements and the
+ * pointers 16-byte aligned.  PAB_UNSUPPORTED for d != 128 or N > 2^20.
+ */
+int64_t pab_attention_backward_workspace(int64_t B, int64_t H, int64_t N, int64_t d);
+pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                  int causal, float sm_scale, const uint8_t* kv_valid,
+                                  const float* out, const int64_t out_strides[4],
+                                  const void* dout, pab_dtype dout_dtype,
+                                  const int64_t dout_strides[4], const float* lse, float* dq,
+                                  float* dk, float* dv, const int64_t grad_strides[4],
+                                  void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * pab_sta_plan - host-side planner for sliding-tile attention [FPS §2.2,

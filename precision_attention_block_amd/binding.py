@@ -21,7 +21,8 @@ TOKEN_ALIGN = 128
 EXPORTS = [
     "pab_abi_version", "pab_status_str", "pab_last_hip_error", "pab_token_alloc",
     "pab_attention_info", "pab_quantize", "pab_attention_dense", "pab_attention_sta",
-    "pab_sta_plan", "pab_count_nonfinite",
+    "pab_sta_plan", "pab_count_nonfinite", "pab_attention_backward_workspace",
+    "pab_attention_backward",
 ]
 
 
@@ -68,11 +69,17 @@ def _lib():
                                    ctypes.c_int64, vp, vp, vp, vp]
         L.pab_attention_dense.restype = ctypes.c_int
         L.pab_attention_dense.argtypes = [ctypes.POINTER(QView)] * 3 + [
-            ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, vp, ctypes.c_int64, vp, i64p, vp]
+            ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, vp, ctypes.c_int64, vp, i64p, vp, vp]
         L.pab_attention_sta.restype = ctypes.c_int
         L.pab_attention_sta.argtypes = [ctypes.POINTER(QView)] * 3 + [
             ctypes.c_float, ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp,
-            ctypes.c_int64, vp, i64p, vp]
+            ctypes.c_int64, vp, i64p, vp, vp]
+        L.pab_attention_backward_workspace.restype = ctypes.c_int64
+        L.pab_attention_backward_workspace.argtypes = [ctypes.c_int64] * 4
+        L.pab_attention_backward.restype = ctypes.c_int
+        L.pab_attention_backward.argtypes = [ctypes.POINTER(QView)] * 3 + [
+            ctypes.c_int, ctypes.c_float, vp, vp, i64p, vp, ctypes.c_int, i64p, vp, vp, vp, vp,
+            i64p, vp, ctypes.c_int64, vp]
         ip = ctypes.POINTER(ctypes.c_int)
         L.pab_sta_plan.restype = ctypes.c_int
         L.pab_sta_plan.argtypes = [ip, ip, ip, ip, vp, vp, vp, vp, vp, vp, i64p, i64p, i64p]
@@ -181,31 +188,43 @@ def _out_tensor(q, n_out, out):
     return out
 
 
+def _lse_tensor(q, lse):
+    import torch
+    if lse is True:
+        return torch.empty((q.B, q.H, q.N), dtype=torch.float32, device=q.codes.device)
+    return lse or None
+
+
 def attention_dense(q, k, v, causal=False, sm_scale=None, kv_valid=None, out_perm=None,
-                    n_out=None, out=None, tau=0):
+                    n_out=None, out=None, tau=0, lse=None):
     """O = softmax(Q K^T sm_scale) V on quantised operands; returns float32
     [B, H, n_out, d] (n_out defaults to N).  tau: softmax rescale threshold
-    (see pab_attention_dense)."""
+    (see pab_attention_dense).  lse: None, True (allocate) or a float32
+    [B, H, N] tensor for the row statistic; when given, returns (O, lse)."""
     n_out = q.N if n_out is None else int(n_out)
     out = _out_tensor(q, n_out, out)
+    lse_t = _lse_tensor(q, lse)
     qv, kv, vv = q.view(), k.view(), v.view()
     st = _lib().pab_attention_dense(
         ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), int(bool(causal)),
         float(sm_scale or 0.0), int(tau),
         ctypes.c_void_p(kv_valid.data_ptr() if kv_valid is not None else 0),
         ctypes.c_void_p(out_perm.data_ptr() if out_perm is not None else 0), n_out,
-        ctypes.c_void_p(out.data_ptr()), _i64(out.stride()), _stream(out.device))
+        ctypes.c_void_p(out.data_ptr()), _i64(out.stride()),
+        ctypes.c_void_p(lse_t.data_ptr() if lse_t is not None else 0), _stream(out.device))
     _check(st, "pab_attention_dense")
-    return out
+    return (out, lse_t) if lse_t is not None else out
 
 
 def attention_sta(q, k, v, plan, sm_scale=None, use_kv_valid=True, use_out_perm=True, n_out=None,
-                  out=None, tau=0):
-    """Sliding-tile attention with a DevicePlan (see sta_plan / DevicePlan)."""
+                  out=None, tau=0, lse=None):
+    """Sliding-tile attention with a DevicePlan (see sta_plan / DevicePlan);
+    lse as in attention_dense."""
     n_out = plan.n_real if n_out is None else int(n_out)
     if not use_out_perm and n_out is None:
         n_out = q.N
     out = _out_tensor(q, n_out, out)
+    lse_t = _lse_tensor(q, lse)
     qv, kv, vv = q.view(), k.view(), v.view()
     st = _lib().pab_attention_sta(
         ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(sm_scale or 0.0), int(tau),
@@ -213,9 +232,44 @@ def attention_sta(q, k, v, plan, sm_scale=None, use_kv_valid=True, use_out_perm=
         ctypes.c_void_p(plan.lpt.data_ptr()), int(plan.n_tiles), int(plan.tile_tokens),
         ctypes.c_void_p(plan.kv_valid.data_ptr() if use_kv_valid else 0),
         ctypes.c_void_p(plan.perm.data_ptr() if use_out_perm else 0), n_out,
-        ctypes.c_void_p(out.data_ptr()), _i64(out.stride()), _stream(out.device))
+        ctypes.c_void_p(out.data_ptr()), _i64(out.stride()),
+        ctypes.c_void_p(lse_t.data_ptr() if lse_t is not None else 0), _stream(out.device))
     _check(st, "pab_attention_sta")
-    return out
+    return (out, lse_t) if lse_t is not None else out
+
+
+def backward_workspace_bytes(B, H, N, d):
+    return int(_lib().pab_attention_backward_workspace(int(B), int(H), int(N), int(d)))
+
+
+def attention_backward(q, k, v, out, dout, lse, causal=False, sm_scale=None, kv_valid=None,
+                       workspace=None, grads=None):
+    """Gradients (dQ, dK, dV), float32 [B, H, N, d], with respect to the
+    dequantised operands of attention_dense (quantisers pass gradients
+    straight through; see pab_attention_backward).  out and lse come from the
+    forward (called without out_perm); dout is float32 or bfloat16."""
+    import torch
+    dev = out.device
+    if workspace is None:
+        workspace = torch.empty(backward_workspace_bytes(q.B, q.H, q.N, q.d), dtype=torch.uint8,
+                                device=dev)
+    if grads is None:
+        grads = tuple(torch.empty((q.B, q.H, q.N, q.d), dtype=torch.float32, device=dev)
+                      for _ in range(3))
+    dq, dk, dv = grads
+    if dk.stride() != dq.stride() or dv.stride() != dq.stride():
+        raise ValueError("dq, dk and dv must share strides")
+    dt = {torch.float32: PAB_F32, torch.bfloat16: PAB_BF16}[dout.dtype]
+    qv, kv, vv = q.view(), k.view(), v.view()
+    st = _lib().pab_attention_backward(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), int(bool(causal)),
+        float(sm_scale or 0.0), ctypes.c_void_p(kv_valid.data_ptr() if kv_valid is not None else 0),
+        ctypes.c_void_p(out.data_ptr()), _i64(out.stride()), ctypes.c_void_p(dout.data_ptr()), dt,
+        _i64(dout.stride()), ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(dq.data_ptr()),
+        ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()), _i64(dq.stride()),
+        ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(dev))
+    _check(st, "pab_attention_backward")
+    return dq, dk, dv
 
 
 class HostPlan:

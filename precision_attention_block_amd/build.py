@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpab.so")
-SOURCES = ["api.cpp", "quant.hip", "attention.hip"]
+SOURCES = ["api.cpp", "quant.hip", "attention.hip", "attention_bwd.hip"]
 # The attention kernel's inputs are finite by contract (scores, exponentials
 # and maxima never see NaN), so its fmax needs no NaN-quieting of operands.
 EXTRA = {"attention.hip": ["-fno-honor-nans"]}

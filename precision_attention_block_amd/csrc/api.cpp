@@ -12,6 +12,7 @@
 #include <numeric>
 
 #include "../../include/pab.h"
+#include "pab_bwd.h"
 #include "pab_internal.h"
 
 namespace {
@@ -218,11 +219,13 @@ pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
 pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab_qview* v,
                                int causal, float sm_scale, int tau, const uint8_t* kv_valid,
                                const int32_t* out_perm, int64_t n_out_tokens, float* out,
-                               const int64_t out_strides[4], void* stream) {
+                               const int64_t out_strides[4], float* lse, void* stream) {
   pab::AttnArgs a;
   pab_status s = fill_attn_args(q, k, v, sm_scale, tau, kv_valid, out_perm, n_out_tokens, out,
                                 out_strides, a);
   if (s != PAB_OK) return s;
+  if (lse && !aligned(lse, 4)) return PAB_INVALID_ARG;
+  a.lse = lse;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32,
                                           v->recipe == PAB_MXFP4_V, causal ? 1 : 0, st),
@@ -234,8 +237,9 @@ pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_q
                              const int32_t* tile_order, int n_tiles, int tile_tokens,
                              const uint8_t* kv_valid, const int32_t* out_perm,
                              int64_t n_out_tokens, float* out, const int64_t out_strides[4],
-                             void* stream) {
+                             float* lse, void* stream) {
   if (!win_off || !win_idx || !tile_order) return PAB_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return PAB_INVALID_ARG;
   if (n_tiles < 1 || tile_tokens < PAB_TOKEN_ALIGN || tile_tokens % PAB_TOKEN_ALIGN)
     return PAB_INVALID_ARG;
   pab::AttnArgs a;
@@ -243,6 +247,7 @@ pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_q
                                 out_strides, a);
   if (s != PAB_OK) return s;
   if ((int64_t)n_tiles * tile_tokens != q->N) return PAB_INVALID_ARG;
+  a.lse = lse;
   a.win_off = win_off;
   a.win_idx = win_idx;
   a.tile_order = tile_order;
@@ -252,6 +257,118 @@ pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_q
   return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32,
                                           v->recipe == PAB_MXFP4_V, 2, st),
                     st);
+}
+
+int64_t pab_attention_backward_workspace(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return -1;
+  int64_t off[13];
+  return pab::bwd_workspace_layout(B * H, round_up(N, PAB_TOKEN_ALIGN), d, off);
+}
+
+pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                  int causal, float sm_scale, const uint8_t* kv_valid,
+                                  const float* out, const int64_t out_strides[4],
+                                  const void* dout, pab_dtype dout_dtype,
+                                  const int64_t dout_strides[4], const float* lse, float* dq,
+                                  float* dk, float* dv, const int64_t grad_strides[4],
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+  pab_status s;
+  if ((s = check_view(q, 0)) != PAB_OK) return s;
+  if ((s = check_view(k, 0)) != PAB_OK) return s;
+  if ((s = check_view(v, 1)) != PAB_OK) return s;
+  if (q->recipe != k->recipe) return PAB_INVALID_ARG;
+  if (q->B != k->B || q->B != v->B || q->H != k->H || q->H != v->H || q->N != k->N ||
+      q->N != v->N || q->d != k->d || q->d != v->d)
+    return PAB_INVALID_ARG;
+  if (q->d != 128 || q->N > ((int64_t)1 << 20)) return PAB_UNSUPPORTED;
+  if (dout_dtype != PAB_F32 && dout_dtype != PAB_BF16) return PAB_INVALID_ARG;
+  if (!out || !out_strides || !dout || !dout_strides || !lse || !dq || !dk || !dv ||
+      !grad_strides || !workspace)
+    return PAB_INVALID_ARG;
+  const int64_t dq_align = dout_dtype == PAB_BF16 ? 8 : 4;
+  for (int i = 0; i < 3; ++i) {
+    if (out_strides[i] < 0 || out_strides[i] % 4 || grad_strides[i] < 0 || grad_strides[i] % 4 ||
+        dout_strides[i] < 0 || dout_strides[i] % dq_align)
+      return PAB_INVALID_ARG;
+  }
+  if (out_strides[3] != 1 || dout_strides[3] != 1 || grad_strides[3] != 1) return PAB_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || !aligned(lse, 4) || !aligned(workspace, 256))
+    return PAB_INVALID_ARG;
+  if (kv_valid && !aligned(kv_valid, 4)) return PAB_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return PAB_INVALID_ARG;
+  const int64_t BH = q->B * q->H, n_alloc = round_up(q->N, PAB_TOKEN_ALIGN);
+  int64_t off[13];
+  if (workspace_bytes < pab::bwd_workspace_layout(BH, n_alloc, q->d, off)) return PAB_INVALID_ARG;
+
+  pab::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = (int)q->B;
+  a.H = (int)q->H;
+  a.N = (int)q->N;
+  a.n_alloc = (int)n_alloc;
+  a.d = (int)q->d;
+  a.sm = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt((float)q->d);
+  a.sm_log2 = a.sm * 1.4426950408889634f;
+  a.causal = causal != 0;
+  a.qk_mx = q->recipe == PAB_MXFP4_D32;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  auto ws16 = [&](int i) { return reinterpret_cast<uint16_t*>(ws + off[i]); };
+  auto ws32 = [&](int i) { return reinterpret_cast<float*>(ws + off[i]); };
+  if (a.qk_mx) {
+    a.q_codes = static_cast<const uint8_t*>(q->codes);
+    a.k_codes = static_cast<const uint8_t*>(k->codes);
+    a.q_mx = static_cast<const uint8_t*>(q->scales);
+    a.k_mx = static_cast<const uint8_t*>(k->scales);
+    a.q_rows = ws16(0);
+    a.k_rows = ws16(1);
+  } else {
+    a.q_val = static_cast<const uint16_t*>(q->operand);
+    a.k_val = static_cast<const uint16_t*>(k->operand);
+    a.q_scale = static_cast<const float*>(q->scales);
+    a.k_scale = static_cast<const float*>(k->scales);
+    a.blk_q = q->block_tokens;
+    a.blk_k = k->block_tokens;
+    a.nblk_q = (int)((n_alloc + a.blk_q - 1) / a.blk_q);
+    a.nblk_k = (int)((n_alloc + a.blk_k - 1) / a.blk_k);
+    a.q_rows = const_cast<uint16_t*>(a.q_val);   // read only
+    a.k_rows = const_cast<uint16_t*>(a.k_val);
+  }
+  a.v_mx = v->recipe == PAB_MXFP4_V;
+  a.v_codes = static_cast<const uint8_t*>(v->codes);
+  if (a.v_mx)
+    a.v_e8 = static_cast<const uint8_t*>(v->scales);
+  else
+    a.v_scale = static_cast<const float*>(v->scales);
+  a.kv_valid = kv_valid;
+  a.o = out;
+  a.o_sb = out_strides[0];
+  a.o_sh = out_strides[1];
+  a.o_sn = out_strides[2];
+  a.dout = dout;
+  a.dout_bf16 = dout_dtype == PAB_BF16;
+  a.do_sb = dout_strides[0];
+  a.do_sh = dout_strides[1];
+  a.do_sn = dout_strides[2];
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.g_sb = grad_strides[0];
+  a.g_sh = grad_strides[1];
+  a.g_sn = grad_strides[2];
+  a.v_rows = ws16(2);
+  a.dos_rows = ws16(3);
+  a.qt = ws16(4);
+  a.kt = ws16(5);
+  a.dot = ws16(6);
+  a.lse_e = ws32(7);
+  a.dd = ws32(8);
+  a.fq = ws32(9);
+  a.fk = ws32(10);
+  a.kvf = ws32(11);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(pab::launch_attention_backward(a, st), st);
 }
 
 pab_status pab_sta_plan(const int grid[3], const int real_grid[3], const int tile[3],

@@ -43,24 +43,14 @@
 //    L2; causal query tiles are issued longest-first (LPT).
 #include "pab_device.h"
 #include "pab_internal.h"
+#include "pab_lds.h"
 
 namespace pab {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-
-// Slot of 16-byte chunk c of row r in a swizzled LDS tile with CPR chunks per
-// row is c ^ swz(r).  Every operand read below has the 16 lanes of one LDS
-// phase read the same chunk index of 16 consecutive rows; the swizzle sends
-// them to 16 disjoint 4-bank groups.
-template <int CPR>
-__device__ constexpr int swz(int row) {
-  return CPR == 16 ? (row & 15) : CPR == 8 ? ((row >> 1) & 7) : CPR == 4 ? ((row >> 2) & 3)
-                                                                          : ((row >> 3) & 1);
-}
 
 template <int D, bool MX, bool V4 = false>
 struct Tile {
@@ -91,25 +81,6 @@ struct Tile {
   static_assert(!V4 || (MX && D == 128), "FP4 P.V runs with MXFP4 Q/K and d = 128");
 };
 
-// Lane offsets of the LDS-DMA copy of a region of rows (16 CPR bytes each,
-// gstride bytes apart in HBM).  Instruction `inst` fills region bytes
-// [1024 inst, 1024 inst + 1024), lane i writing 16 bytes at 1024 inst + 16 i
-// and fetching the global chunk that belongs in that slot.  The swizzle of
-// row inst * RPI + lane / CPR depends on inst only through inst % PER.
-template <int CPR>
-struct DmaPlan {
-  static constexpr int RPI = 64 / CPR;                            // rows per instruction
-  static constexpr int PER = CPR == 16 ? 4 : CPR == 8 ? 2 : 1;    // swizzle period
-  uint32_t off[PER];
-  __device__ void init(int lane, int64_t gstride) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int row = p * RPI + lane / CPR;
-      off[p] = (uint32_t)((lane / CPR) * gstride + 16 * ((lane % CPR) ^ swz<CPR>(row)));
-    }
-  }
-};
-
 #if defined(__HIP_DEVICE_COMPILE__)
 // (buffer descriptors and everything that uses them exist in the device pass only)
 struct HeadBuffers {
@@ -117,7 +88,6 @@ struct HeadBuffers {
   bool has_mask;
   int blk_k;
 };
-constexpr int kRsrcWord3 = 0x00020000;   // raw byte buffer
 
 // Every wave issues the same number of LDS-DMA instructions per copy (K for
 // a K stage, V for a V stage plus a side stage), and every pipeline iteration
@@ -193,24 +163,6 @@ __device__ inline void issue_aux(uint8_t* abuf, const HeadBuffers& hb, int ks, i
   if (!MX)   // scales of the blocks from ks / blk on (a tile spans at most 4)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.c, (lds_void_t*)(abuf + TL::M_BYTES), 4, 4 * lane,
                                              (ks / hb.blk_k) * 4, 0, 0);
-}
-
-// Workgroup barrier that does not wait for outstanding LDS-DMA copies (a
-// plain __syncthreads() fences every memory operation, including the copies
-// that are meant to stay in flight); this wave's LDS reads are complete first.
-// The waits use the s_waitcnt builtin (simm16: vmcnt bits 3:0 and 15:14,
-// expcnt 6:4, lgkmcnt 11:8) rather than inline asm so that the compiler's own
-// wait-count tracking sees them and adds no conservative waits of its own.
-__device__ inline void barrier_lds() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt untouched
-  __builtin_amdgcn_s_barrier();
-}
-
-// Waits until at most N of this wave's LDS-DMA copies are outstanding.
-template <int N>
-__device__ inline void wait_vm_le() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 __device__ inline v8i make_v8(uint4 lo, uint4 hi) {
@@ -783,6 +735,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const float lt = swap_sum(l_run);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (myq < a.N) {
+    // row statistic for the backward pass: LSE = m + log2(sum_j 2^(S_j - m));
+    // l carries the factor 448 / 2^tau of the FP8 P (FP4 P.V: none)
+    if (a.lse && lg == 0)
+      a.lse[(int64_t)bh * a.N + myq] =
+          lt > 0.0f ? m_run + __log2f(lt) - (V4 ? 0.0f : kLog2_448 - a.tau) : kNegInf;
     const int tok = a.out_perm ? a.out_perm[myq] : myq;
     if (tok >= 0) {
       const int b = bh / a.H, h = bh % a.H;
@@ -1247,6 +1204,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   const float lt = swap_sum(l_run);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (myq < a.N) {
+    if (a.lse && lg == 0)   // as in the 4-wave kernel
+      a.lse[(int64_t)bh * a.N + myq] = lt > 0.0f ? m_run + __log2f(lt) - (kLog2_448 - a.tau) : kNegInf;
     const int tok = a.out_perm ? a.out_perm[myq] : myq;
     if (tok >= 0) {
       const int b = bh / a.H, h = bh % a.H;

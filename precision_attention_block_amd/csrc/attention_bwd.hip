@@ -1,0 +1,585 @@
+// Attention backward pass for gfx950 (CDNA4).
+//
+// The FA4 page ("FA4极速LLM：10分钟搞定20倍内存直降！", co-design list: the
+// backward pass and its intermediates S, P, dP, dS, dQ) and the FPSAttention
+// page ("FP8量化与稀疏性协同加速视频扩散模型", introduction: training-aware FP8)
+// fix what is computed up to the gradient of the quantisers, which passes
+// straight through: with the dequantised operands Q^, K^, V^ of the forward
+// pass, its output O and its row statistic LSE (log2 units),
+//   P = 2^(S log2 e - LSE), S = Q^ K^T sm     dV^ = P^T dO
+//   dP = dO V^^T    D_i = sum_c dO_ic O_ic    dS = P (dP - D)
+//   dQ^ = sm dS K^  dK^ = sm dS^T Q^
+// The products run on v_mfma_f32_32x32x16_bf16.  Q and K enter as the exact
+// bf16 values of their codes (FP8) or as exactly dequantised values (MXFP4),
+// with the FP8 block scales applied in fp32 to S and folded into dS; V enters
+// as exact code values with its per-channel FP8 scale folded into dO.  P, dS
+// and dO are rounded to bf16 for their products; every sum is fp32.
+//
+// Two kernels, FlashAttention-2 style, so no atomics and a deterministic sum
+// order:
+//  * dK/dV: a workgroup owns 128 keys (4 waves x 32); each wave keeps the K
+//    and V rows of its keys in registers as B operands and walks the queries
+//    in steps of 32.
+//  * dQ: a workgroup owns 128 queries; each wave keeps the Q and dO rows of
+//    its queries in registers and walks the keys in steps of 32.
+// In the 32x32 MFMA result layout a lane holds one column and 16 rows
+// 8 i + 4 lg + r (i, r < 4, lg = lane / 32).  Registers 8h .. 8h+7 of a
+// score tile are therefore exactly the B operand of the next product over
+// the rows 16h .. 16h+15 when the other operand lists those rows with bits 2
+// and 3 of the index swapped.  The prep kernels write Q^T, K^T and dO^T in
+// that order ("block transpose" done ahead of the kernel, as the forward's V),
+// so the scores never leave the registers.
+// Tiles reach LDS by LDS-DMA into XOR-swizzled rows (conflict-free 16-byte
+// operand reads), one step ahead of the step being computed.
+#include "pab_bwd.h"
+#include "pab_device.h"
+#include "pab_lds.h"
+
+namespace pab {
+
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+
+constexpr float kInf = __builtin_huge_valf();
+constexpr int kD = 128;
+
+int64_t bwd_workspace_layout(int64_t BH, int64_t n_alloc, int64_t d, int64_t off[13]) {
+  const int64_t rows = BH * n_alloc * d * 2, toks = BH * n_alloc * 4;
+  const int64_t sizes[12] = {rows, rows, rows, rows, rows, rows, rows, toks, toks, toks, toks,
+                             n_alloc * 4};
+  int64_t at = 0;
+  for (int i = 0; i < 12; ++i) {
+    off[i] = at;
+    at += (sizes[i] + 255) / 256 * 256;
+  }
+  off[12] = at;
+  return at;
+}
+
+// Token index with bits 2 and 3 swapped (an involution): the slot of token t
+// in a transposed array, and the token of slot t.
+__device__ constexpr int swap23(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+
+__device__ inline uint32_t bf16x2(float a, float b) {   // round to nearest even
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v{a, b}, b2v));
+}
+// two floats whose values are exact in bf16
+__device__ inline uint32_t bf16x2_exact(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
+
+// E2M1 code (4 bits) -> its value: 0, 0.5, 1, 1.5, 2, 3, 4, 6 with sign bit 3
+// ("Blackwell架构实战……", §1: E2M1).
+__device__ inline float e2m1_value(uint32_t nib) {
+  const uint32_t m = nib & 7;
+  const uint32_t mag = m < 2 ? (m ? 0x3F000000u : 0u) : (((126u + (m >> 1)) << 23) | ((m & 1) << 22));
+  return __uint_as_float(mag | ((nib & 8) << 28));
+}
+
+// Writes the transposed copy of a 64-token x 128-channel bf16 tile (row pitch
+// TP elements) to dst[c * n_alloc + slot], slots in swap23 order.
+template <int TP>
+__device__ inline void store_transposed(const uint16_t* tile, uint16_t* dst, int n_alloc, int tid) {
+  for (int u = tid; u < kD * 8; u += 256) {
+    const int c = u / 8, ch = u % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s0 = 8 * ch + 2 * j;
+      w[j] = (uint32_t)tile[swap23(s0) * TP + c] | ((uint32_t)tile[swap23(s0 + 1) * TP + c] << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + (int64_t)c * n_alloc + 8 * ch) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---- prep: Q / K values, their transposed copies and per-token factors -----
+// grid (n_alloc / 64, BH, 2): z = 0 Q, 1 K.
+template <bool MX>
+__global__ __launch_bounds__(256) void bwd_prep_qk_kernel(BwdArgs a) {
+  constexpr int TP = kD + 8;
+  __shared__ __align__(16) uint16_t tile[64 * TP];
+  const int bh = blockIdx.y, t0 = blockIdx.x * 64, tid = threadIdx.x;
+  const bool isk = blockIdx.z == 1;
+  const int64_t tokb = (int64_t)bh * a.n_alloc + t0;
+  for (int u = tid; u < 64 * 16; u += 256) {
+    const int t = u / 16, c8 = u % 16;
+    uint4 w;
+    if (MX) {
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>((isk ? a.k_codes : a.q_codes) +
+                                                             (tokb + t) * (kD / 2) + 4 * c8);
+      const int e8 = (isk ? a.k_mx : a.q_mx)[(tokb + t) * (kD / 32) + c8 / 4];
+      const float sc = __builtin_amdgcn_ldexpf(1.0f, e8 - 127);
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e2m1_value((cw >> (4 * j)) & 15) * sc;
+      w = make_uint4(bf16x2_exact(v[0], v[1]), bf16x2_exact(v[2], v[3]), bf16x2_exact(v[4], v[5]),
+                     bf16x2_exact(v[6], v[7]));
+      *reinterpret_cast<uint4*>((isk ? a.k_rows : a.q_rows) + (tokb + t) * kD + 8 * c8) = w;
+    } else {
+      w = *reinterpret_cast<const uint4*>((isk ? a.k_val : a.q_val) + (tokb + t) * kD + 8 * c8);
+    }
+    *reinterpret_cast<uint4*>(&tile[t * TP + 8 * c8]) = w;
+  }
+  if (tid < 64) {
+    float f = 1.0f;
+    if (!MX) {
+      const int t = t0 + tid;
+      f = 1.0f / (isk ? a.k_scale[(int64_t)bh * a.nblk_k + t / a.blk_k]
+                      : a.q_scale[(int64_t)bh * a.nblk_q + t / a.blk_q]);
+    }
+    (isk ? a.fk : a.fq)[tokb + tid] = f;
+  }
+  __syncthreads();
+  store_transposed<TP>(tile, (isk ? a.kt : a.qt) + (int64_t)bh * kD * a.n_alloc + t0, a.n_alloc, tid);
+}
+
+// ---- prep: V values as bf16 rows ---------------------------------------------
+// grid (n_alloc / 64, BH).  FP8: the exact values of the E4M3 codes (the
+// channel scale is folded into dO); MXFP4: the exactly dequantised values.
+template <bool MXV>
+__global__ __launch_bounds__(256) void bwd_prep_v_kernel(BwdArgs a) {
+  constexpr int RP = 80;   // LDS row pitch (bytes) of a channel
+  __shared__ __align__(16) uint8_t tile[kD * RP];
+  __shared__ uint8_t e8[2 * kD];
+  const int bh = blockIdx.y, t0 = blockIdx.x * 64, tid = threadIdx.x;
+  if (!MXV) {
+    for (int u = tid; u < kD * 4; u += 256) {
+      const int c = u / 4, ch = u % 4;
+      *reinterpret_cast<uint4*>(tile + c * RP + 16 * ch) = *reinterpret_cast<const uint4*>(
+          a.v_codes + ((int64_t)bh * kD + c) * a.n_alloc + t0 + 16 * ch);
+    }
+  } else {
+    for (int u = tid; u < kD * 2; u += 256) {
+      const int c = u / 2, ch = u % 2;
+      *reinterpret_cast<uint4*>(tile + c * RP + 16 * ch) = *reinterpret_cast<const uint4*>(
+          a.v_codes + ((int64_t)bh * kD + c) * (a.n_alloc / 2) + t0 / 2 + 16 * ch);
+    }
+    e8[tid] = a.v_e8[((int64_t)bh * (a.n_alloc / 32) + t0 / 32) * kD + tid];
+  }
+  __syncthreads();
+  uint16_t* out = a.v_rows + ((int64_t)bh * a.n_alloc + t0) * kD;
+  for (int u = tid; u < 64 * 16; u += 256) {
+    const int t = u / 16, c8 = u % 16;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 8 * c8 + 2 * j;
+      if (!MXV) {
+        // the V quantizer's 64-token interleave: quad lq of the group sits at
+        // 32 (lq % 2) + 16 (lq / 8) + 4 ((lq % 8) / 2)
+        const int lq = t / 4;
+        const int slot = 32 * (lq % 2) + 16 * (lq / 8) + 4 * ((lq % 8) / 2) + t % 4;
+        w[j] = e4m3_bf16x2<false>((uint32_t)tile[c * RP + slot] | ((uint32_t)tile[(c + 1) * RP + slot] << 8));
+      } else {
+        // 32-token groups: token 8 a + 4 b + r sits at slot 16 b + 4 a + r,
+        // two slots per byte, the even slot in the low nibble
+        const int g = t / 32, tt = t % 32;
+        const int slot = 16 * ((tt / 4) % 2) + 4 * (tt / 8) + tt % 4;
+        float v2[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const uint32_t byte = tile[(c + x) * RP + 16 * g + slot / 2];
+          const int e = e8[g * kD + 4 * ((c + x) % 32) + (c + x) / 32];
+          v2[x] = e2m1_value((slot & 1) ? byte >> 4 : byte & 15) * __builtin_amdgcn_ldexpf(1.0f, e - 127);
+        }
+        w[j] = bf16x2_exact(v2[0], v2[1]);
+      }
+    }
+    *reinterpret_cast<uint4*>(out + (int64_t)t * kD + 8 * c8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---- prep: dO rows and dO^T, D = rowsum(dO * O), LSE and key validity -------
+// grid (n_alloc / 64, BH).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_prep_do_kernel(BwdArgs a) {
+  constexpr int TP = kD + 8;
+  __shared__ __align__(16) uint16_t tile[64 * TP];
+  __shared__ float fv[kD];
+  const int bh = blockIdx.y, t0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int b = bh / a.H, h = bh % a.H;
+  if (tid < kD) fv[tid] = a.v_mx ? 1.0f : 1.0f / a.v_scale[(int64_t)bh * kD + tid];
+  __syncthreads();
+  const int t = tid / 4, part = tid % 4, tok = t0 + t;
+  const bool live = tok < a.N;
+  const T* g = static_cast<const T*>(a.dout) + b * a.do_sb + h * a.do_sh + (int64_t)(live ? tok : 0) * a.do_sn;
+  const float* o = a.o + b * a.o_sb + h * a.o_sh + (int64_t)(live ? tok : 0) * a.o_sn;
+  uint16_t* drow = a.dos_rows + ((int64_t)bh * a.n_alloc + tok) * kD;
+  float acc = 0.0f;
+#pragma unroll
+  for (int c8 = 0; c8 < 4; ++c8) {
+    const int c0 = 32 * part + 8 * c8;
+    float gv[8], ov[8];
+    if (live) {
+      load8(g + c0, gv);
+      load8(o + c0, ov);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) gv[j] = ov[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf(gv[j], ov[j], acc);
+    uint32_t ws[4], wt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ws[j] = bf16x2(gv[2 * j] * fv[c0 + 2 * j], gv[2 * j + 1] * fv[c0 + 2 * j + 1]);
+      wt[j] = bf16x2(gv[2 * j], gv[2 * j + 1]);
+    }
+    *reinterpret_cast<uint4*>(drow + c0) = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+    *reinterpret_cast<uint4*>(&tile[t * TP + c0]) = make_uint4(wt[0], wt[1], wt[2], wt[3]);
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  if (part == 0) {
+    const int64_t at = (int64_t)bh * a.n_alloc + tok;
+    a.dd[at] = live ? acc : 0.0f;
+    const float l = live ? a.lse[(int64_t)bh * a.N + tok] : kInf;
+    a.lse_e[at] = l == -kInf ? kInf : l;   // a row without a valid key: every P is 0
+    if (bh == 0) a.kvf[tok] = (live && (!a.kv_valid || a.kv_valid[tok])) ? 1.0f : 0.0f;
+  }
+  __syncthreads();
+  store_transposed<TP>(tile, a.dot + (int64_t)bh * kD * a.n_alloc + t0, a.n_alloc, tid);
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// LDS stage of one 32-token step: two row tiles [32][256 B] (CPR 16), one or
+// two transposed tiles [128][64 B] (CPR 4) and 256-byte copies of per-token
+// floats (32 used).
+struct Stage {
+  static constexpr int R0 = 0, R1 = 8192, T0 = 16384, T1 = 24576, F0 = 32768, F1 = F0 + 256,
+                       F2 = F1 + 256, BYTES = F2 + 256;
+};
+
+__device__ inline v8s lds_row_operand(const uint8_t* base, int row, int chunk) {
+  return *reinterpret_cast<const v8s*>(base + row * 256 + 16 * (chunk ^ swz<16>(row)));
+}
+__device__ inline v8s lds_t_operand(const uint8_t* base, int row, int chunk) {
+  return *reinterpret_cast<const v8s*>(base + row * 64 + 16 * (chunk ^ swz<4>(row)));
+}
+
+// Copies of one step: 8 KB row tiles take 8 instructions of 1 KB (4 rows),
+// 8 KB transposed tiles 8 instructions (16 rows); each wave issues 2 of each
+// tile's 8.  The per-token floats are one full-wave dword copy each, issued
+// by every wave to the same place.
+__device__ inline void issue_rows(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int t0, int wave,
+                                  const DmaPlan<16>& pr) {
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int inst = 2 * wave + x;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + inst * 1024), 16, pr.off[inst % 4],
+                                             (t0 + 4 * inst) * 2 * kD, 0, 0);
+  }
+}
+__device__ inline void issue_trans(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int t0, int n_alloc,
+                                   int wave, const DmaPlan<4>& pt) {
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int inst = 2 * wave + x;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + inst * 1024), 16, pt.off[0],
+                                             t0 * 2 + inst * 16 * 2 * n_alloc, 0, 0);
+  }
+}
+__device__ inline void issue_floats(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int t0, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 4, 4 * lane, t0 * 4, 0, 0);
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
+}
+
+// Packs registers 8h .. 8h+7 of a score tile into a bf16 B operand.
+__device__ inline v8s pack_b(const float (&x)[16], int h) {
+  return __builtin_bit_cast(v8s, make_uint4(bf16x2(x[8 * h], x[8 * h + 1]), bf16x2(x[8 * h + 2], x[8 * h + 3]),
+                                            bf16x2(x[8 * h + 4], x[8 * h + 5]),
+                                            bf16x2(x[8 * h + 6], x[8 * h + 7])));
+}
+#endif  // __HIP_DEVICE_COMPILE__
+
+// ---- dK, dV --------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __align__(16) uint8_t st0[Stage::BYTES], st1[Stage::BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lg = lane >> 5;
+  const int n_kt = a.n_alloc / kBwdTile;
+  const int work = xcd_work_index(blockIdx.x, gridDim.x);
+  const int bh = work / n_kt, kt = work % n_kt;
+  const int key0 = kt * kBwdTile + 32 * wave;   // this wave's 32 keys
+  const int j = key0 + lr;                      // this lane's key
+  const int64_t tokb = (int64_t)bh * a.n_alloc;
+
+  // K and V rows of key j as B operands: k-step s holds channels 16 s + 8 lg .. + 7
+  v8s kb[8], vb[8];
+  {
+    const uint4* kr = reinterpret_cast<const uint4*>(a.k_rows + (tokb + j) * kD);
+    const uint4* vr = reinterpret_cast<const uint4*>(a.v_rows + (tokb + j) * kD);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kb[s] = __builtin_bit_cast(v8s, kr[2 * s + lg]);
+      vb[s] = __builtin_bit_cast(v8s, vr[2 * s + lg]);
+    }
+  }
+  const float ck = a.sm_log2 * a.fk[tokb + j];
+  const bool kvalid = a.kvf[j] != 0.0f;
+  const bool all_valid = __all(kvalid);
+
+  const auto qr = rsrc(a.q_rows + tokb * kD, (int64_t)a.n_alloc * kD * 2);
+  const auto dr = rsrc(a.dos_rows + tokb * kD, (int64_t)a.n_alloc * kD * 2);
+  const auto qtr = rsrc(a.qt + tokb * kD, (int64_t)a.n_alloc * kD * 2);
+  const auto dtr = rsrc(a.dot + tokb * kD, (int64_t)a.n_alloc * kD * 2);
+  const auto lsr = rsrc(a.lse_e + tokb, (int64_t)a.n_alloc * 4);
+  const auto ddr = rsrc(a.dd + tokb, (int64_t)a.n_alloc * 4);
+  const auto fqr = rsrc(a.fq + tokb, (int64_t)a.n_alloc * 4);
+  DmaPlan<16> pr;
+  pr.init(lane, 2 * kD);
+  DmaPlan<4> pt;
+  pt.init(lane, 2 * (int64_t)a.n_alloc);
+  auto issue = [&](uint8_t* stg, int q0) __attribute__((always_inline)) {
+    issue_rows(qr, stg + Stage::R0, q0, wave, pr);
+    issue_rows(dr, stg + Stage::R1, q0, wave, pr);
+    issue_trans(qtr, stg + Stage::T0, q0, a.n_alloc, wave, pt);
+    issue_trans(dtr, stg + Stage::T1, q0, a.n_alloc, wave, pt);
+    issue_floats(lsr, stg + Stage::F0, q0, lane);
+    issue_floats(ddr, stg + Stage::F1, q0, lane);
+    issue_floats(fqr, stg + Stage::F2, q0, lane);
+  };
+
+  v16f dvt[4], dkt[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dvt[cb][e] = dkt[cb][e] = 0.0f;
+
+  const int q_begin = CAUSAL ? kt * kBwdTile : 0;   // earlier queries see none of these keys
+  const int q_end = (a.N + 31) / 32 * 32;
+  issue(st0, q_begin);
+  int it = 0;
+  for (int q0 = q_begin; q0 < q_end; q0 += 32, ++it) {
+    const uint8_t* cur = (it & 1) ? st1 : st0;
+    wait_vm_le<0>();
+    barrier_lds();   // this step has landed everywhere; every wave is done with the other stage
+    if (q0 + 32 < q_end) issue((it & 1) ? st0 : st1, q0 + 32);
+    if (CAUSAL && q0 + 32 <= key0) continue;   // every query of the step precedes this wave's keys
+
+    // S (queries x keys) = Q K^T and dP = (dO / s_V) V_codes^T
+    v16f s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R0, lr, 2 * ks + lg), kb[ks], s,
+                                                  0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R1, lr, 2 * ks + lg), vb[ks],
+                                                   dp, 0, 0, 0);
+    }
+    // register 4 i + r is query q0 + 8 i + 4 lg + r
+    float4 ls4[4], dd4[4], fq4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ls4[i] = *reinterpret_cast<const float4*>(cur + Stage::F0 + 4 * (8 * i + 4 * lg));
+      dd4[i] = *reinterpret_cast<const float4*>(cur + Stage::F1 + 4 * (8 * i + 4 * lg));
+      fq4[i] = *reinterpret_cast<const float4*>(cur + Stage::F2 + 4 * (8 * i + 4 * lg));
+    }
+    const bool masked = !all_valid || (CAUSAL && q0 < key0 + 32);
+    float p[16], ds[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = e / 4, r = e % 4;
+      const float lse = r == 0 ? ls4[i].x : r == 1 ? ls4[i].y : r == 2 ? ls4[i].z : ls4[i].w;
+      const float dd = r == 0 ? dd4[i].x : r == 1 ? dd4[i].y : r == 2 ? dd4[i].z : dd4[i].w;
+      const float fq = r == 0 ? fq4[i].x : r == 1 ? fq4[i].y : r == 2 ? fq4[i].z : fq4[i].w;
+      float pe = __builtin_amdgcn_exp2f(fmaf(s[e] * ck, fq, -lse));
+      if (masked) {
+        const int q = q0 + 8 * i + 4 * lg + r;
+        pe = (kvalid && (!CAUSAL || q >= j)) ? pe : 0.0f;
+      }
+      p[e] = pe;
+      ds[e] = pe * (dp[e] - dd) * (a.sm * fq);   // dS scaled for dK^ = sm dS^T Q^
+    }
+    // dV^T += dO^T P and dK^T += Q_vals^T dS' (channels x keys, K = queries)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v8s pb = pack_b(p, h), dsb = pack_b(ds, h);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int row = 32 * cb + lr;
+        dvt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T1, row, 2 * h + lg), pb,
+                                                          dvt[cb], 0, 0, 0);
+        dkt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T0, row, 2 * h + lg), dsb,
+                                                          dkt[cb], 0, 0, 0);
+      }
+    }
+  }
+  wait_vm_le<0>();   // no copy may still target this workgroup's LDS when it ends
+  // lane (key j, lg) holds channels 32 cb + 8 i + 4 lg + r
+  if (j < a.N) {
+    const int b = bh / a.H, h = bh % a.H;
+    float* dvrow = a.dv + b * a.g_sb + h * a.g_sh + (int64_t)j * a.g_sn;
+    float* dkrow = a.dk + b * a.g_sb + h * a.g_sh + (int64_t)j * a.g_sn;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c0 = 32 * cb + 8 * i + 4 * lg;
+        *reinterpret_cast<float4*>(dvrow + c0) =
+            make_float4(dvt[cb][4 * i], dvt[cb][4 * i + 1], dvt[cb][4 * i + 2], dvt[cb][4 * i + 3]);
+        *reinterpret_cast<float4*>(dkrow + c0) =
+            make_float4(dkt[cb][4 * i], dkt[cb][4 * i + 1], dkt[cb][4 * i + 2], dkt[cb][4 * i + 3]);
+      }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// ---- dQ -------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __align__(16) uint8_t st0[Stage::BYTES], st1[Stage::BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lg = lane >> 5;
+  const int n_qt = a.n_alloc / kBwdTile;
+  const int work = xcd_work_index(blockIdx.x, gridDim.x);
+  const int bh = work / n_qt;
+  int qt = work % n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;               // longest query tiles first
+  const int qw0 = qt * kBwdTile + 32 * wave;     // this wave's 32 queries
+  const int i = qw0 + lr;                        // this lane's query
+  const int64_t tokb = (int64_t)bh * a.n_alloc;
+
+  v8s qb[8], gb[8];
+  {
+    const uint4* qr = reinterpret_cast<const uint4*>(a.q_rows + (tokb + i) * kD);
+    const uint4* gr = reinterpret_cast<const uint4*>(a.dos_rows + (tokb + i) * kD);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qb[s] = __builtin_bit_cast(v8s, qr[2 * s + lg]);
+      gb[s] = __builtin_bit_cast(v8s, gr[2 * s + lg]);
+    }
+  }
+  const float cq = a.sm_log2 * a.fq[tokb + i];
+  const float lse = a.lse_e[tokb + i];
+  const float ddi = a.dd[tokb + i];
+
+  const auto kr = rsrc(a.k_rows + tokb * kD, (int64_t)a.n_alloc * kD * 2);
+  const auto vr = rsrc(a.v_rows + tokb * kD, (int64_t)a.n_alloc * kD * 2);
+  const auto ktr = rsrc(a.kt + tokb * kD, (int64_t)a.n_alloc * kD * 2);
+  const auto fkr = rsrc(a.fk + tokb, (int64_t)a.n_alloc * 4);
+  const auto kvr = rsrc(a.kvf, (int64_t)a.n_alloc * 4);
+  DmaPlan<16> pr;
+  pr.init(lane, 2 * kD);
+  DmaPlan<4> pt;
+  pt.init(lane, 2 * (int64_t)a.n_alloc);
+  auto issue = [&](uint8_t* stg, int k0) __attribute__((always_inline)) {
+    issue_rows(kr, stg + Stage::R0, k0, wave, pr);
+    issue_rows(vr, stg + Stage::R1, k0, wave, pr);
+    issue_trans(ktr, stg + Stage::T0, k0, a.n_alloc, wave, pt);
+    issue_floats(fkr, stg + Stage::F0, k0, lane);
+    issue_floats(kvr, stg + Stage::F1, k0, lane);
+  };
+
+  v16f dqt[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqt[cb][e] = 0.0f;
+
+  const int n_keys = (a.N + 31) / 32 * 32;
+  const int k_end = CAUSAL ? min(qt * kBwdTile + kBwdTile, n_keys) : n_keys;
+  const bool tail_mask = a.kv_valid != nullptr;
+  issue(st0, 0);
+  int it = 0;
+  for (int k0 = 0; k0 < k_end; k0 += 32, ++it) {
+    const uint8_t* cur = (it & 1) ? st1 : st0;
+    wait_vm_le<0>();
+    barrier_lds();
+    if (k0 + 32 < k_end) issue((it & 1) ? st0 : st1, k0 + 32);
+    if (CAUSAL && k0 > qw0 + 31) continue;   // every key of the step follows this wave's queries
+
+    // S^T (keys x queries) = K Q^T and dP^T = V_codes (dO / s_V)^T
+    v16f s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R0, lr, 2 * ks + lg), qb[ks], s,
+                                                  0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R1, lr, 2 * ks + lg), gb[ks],
+                                                   dp, 0, 0, 0);
+    }
+    // register 4 ii + r is key k0 + 8 ii + 4 lg + r
+    float4 fk4[4], kv4[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      fk4[ii] = *reinterpret_cast<const float4*>(cur + Stage::F0 + 4 * (8 * ii + 4 * lg));
+      kv4[ii] = *reinterpret_cast<const float4*>(cur + Stage::F1 + 4 * (8 * ii + 4 * lg));
+    }
+    const bool masked = tail_mask || k0 + 32 > a.N || (CAUSAL && k0 + 31 > qw0);
+    float ds[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int ii = e / 4, r = e % 4;
+      const float fk = r == 0 ? fk4[ii].x : r == 1 ? fk4[ii].y : r == 2 ? fk4[ii].z : fk4[ii].w;
+      float pe = __builtin_amdgcn_exp2f(fmaf(s[e] * cq, fk, -lse));
+      if (masked) {
+        const float kv = r == 0 ? kv4[ii].x : r == 1 ? kv4[ii].y : r == 2 ? kv4[ii].z : kv4[ii].w;
+        const int key = k0 + 8 * ii + 4 * lg + r;
+        pe = (kv != 0.0f && (!CAUSAL || key <= i)) ? pe : 0.0f;
+      }
+      ds[e] = pe * (dp[e] - ddi) * (a.sm * fk);   // dS scaled for dQ^ = sm dS K^
+    }
+    // dQ^T += K_vals^T dS'^T (channels x queries, K = keys)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v8s dsb = pack_b(ds, h);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        dqt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T0, 32 * cb + lr, 2 * h + lg),
+                                                          dsb, dqt[cb], 0, 0, 0);
+    }
+  }
+  wait_vm_le<0>();
+  if (i < a.N) {
+    const int b = bh / a.H, h = bh % a.H;
+    float* row = a.dq + b * a.g_sb + h * a.g_sh + (int64_t)i * a.g_sn;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        *reinterpret_cast<float4*>(row + 32 * cb + 8 * ii + 4 * lg) =
+            make_float4(dqt[cb][4 * ii], dqt[cb][4 * ii + 1], dqt[cb][4 * ii + 2], dqt[cb][4 * ii + 3]);
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+hipError_t launch_attention_backward(const BwdArgs& a, hipStream_t st) {
+  const unsigned BH = (unsigned)(a.B * a.H);
+  const dim3 g64((unsigned)(a.n_alloc / 64), BH);
+  if (a.qk_mx)
+    hipLaunchKernelGGL(bwd_prep_qk_kernel<true>, dim3(g64.x, g64.y, 2), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(bwd_prep_qk_kernel<false>, dim3(g64.x, g64.y, 2), dim3(256), 0, st, a);
+  if (a.v_mx)
+    hipLaunchKernelGGL(bwd_prep_v_kernel<true>, g64, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(bwd_prep_v_kernel<false>, g64, dim3(256), 0, st, a);
+  if (a.dout_bf16)
+    hipLaunchKernelGGL(bwd_prep_do_kernel<__hip_bfloat16>, g64, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(bwd_prep_do_kernel<float>, g64, dim3(256), 0, st, a);
+  const dim3 gt(BH * (unsigned)(a.n_alloc / kBwdTile));
+  if (a.causal) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, gt, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, gt, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, gt, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, gt, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pab

@@ -41,6 +41,7 @@ struct AttnArgs {
   const int32_t* out_perm;    // nullable, [N]
   float* out;
   int64_t osb, osh, osn;      // output element strides (channel stride 1)
+  float* lse;                 // nullable, [BH][N]: log2-sum-exp row statistic (kernel order)
   int B, H, N, n_alloc;
   int blk_q, blk_k, nblk_q, nblk_k;
   float sm_log2;          // sm_scale * log2(e)

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(B):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(B.lib(), name), name
-    assert B.lib().pab_abi_version() == 2
+    assert B.lib().pab_abi_version() == 3
 
 
 def test_token_alloc_and_info(B):
@@ -104,9 +104,9 @@ def test_attention_validation_without_device(B):
     out_str = B._i64([2 * 256 * 128, 256 * 128, 128, 1])
     null = ctypes.c_void_p(0)
     f = ctypes.c_void_p(fake)
-    dense = lambda q, k, v, strides=out_str, n_out=256, sm=0.0, tau=0: L.pab_attention_dense(
+    dense = lambda q, k, v, strides=out_str, n_out=256, sm=0.0, tau=0, lse=null: L.pab_attention_dense(
         ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, sm, tau, null, null, n_out, f, strides,
-        null)
+        lse, null)
     assert dense(qv, kv, mk(0)) == B.PAB_INVALID_ARG          # V with the Q/K recipe
     assert dense(qv, mk(2), vv) == B.PAB_INVALID_ARG          # mixed Q/K recipes
     assert dense(qv, mk(0, n=300), vv) == B.PAB_INVALID_ARG   # shape mismatch
@@ -118,15 +118,45 @@ def test_attention_validation_without_device(B):
     assert dense(qv, kv, vv, tau=9) == B.PAB_INVALID_ARG
     bad = B._i64([2 * 256 * 128, 256 * 128, 130, 1])
     assert dense(qv, kv, vv, strides=bad) == B.PAB_INVALID_ARG
+    assert dense(qv, kv, vv, lse=ctypes.c_void_p(fake + 2)) == B.PAB_INVALID_ARG   # misaligned lse
     sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, 0, f, f, f,
-                              2, 100, null, null, 256, f, out_str, null)
+                              2, 100, null, null, 256, f, out_str, null, null)
     assert sta == B.PAB_INVALID_ARG                           # tile not a multiple of 128
     sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, 0, f, f, f,
-                              3, 128, null, null, 256, f, out_str, null)
+                              3, 128, null, null, 256, f, out_str, null, null)
     assert sta == B.PAB_INVALID_ARG                           # tiles do not cover N
     sta = L.pab_attention_sta(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, 12, f, f, f,
-                              2, 128, null, null, 256, f, out_str, null)
+                              2, 128, null, null, 256, f, out_str, null, null)
     assert sta == B.PAB_INVALID_ARG                           # rescale threshold out of range
+    assert L.pab_last_hip_error() == 0
+
+
+def test_backward_validation_without_device(B):
+    L = B.lib()
+    fake = 4096
+    mk = lambda recipe, n=256, d=128, blk=128, op=fake: B.QView(fake, fake, op, recipe, blk, 1, 2, n, d)
+    qv, kv, vv = mk(0), mk(0), mk(1)
+    st = B._i64([2 * 256 * 128, 256 * 128, 128, 1])
+    null = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(fake)
+    need = L.pab_attention_backward_workspace(1, 2, 256, 128)
+    # seven bf16 [BH, n_alloc, d] arrays, four float32 [BH, n_alloc], one float32 [n_alloc]
+    assert need == 7 * 2 * 256 * 128 * 2 + 4 * 2 * 256 * 4 + 256 * 4
+    assert L.pab_attention_backward_workspace(0, 2, 256, 128) < 0
+
+    def bwd(q=qv, k=kv, v=vv, ws=fake * 16, nbytes=need, dt=B.PAB_F32, lse=f, gstr=st, dstr=st):
+        return L.pab_attention_backward(
+            ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, 0.0, null, f, st, f, dt, dstr,
+            lse, f, f, f, gstr, ctypes.c_void_p(ws), nbytes, null)
+    assert bwd(nbytes=need - 1) == B.PAB_INVALID_ARG                 # workspace too small
+    assert bwd(ws=fake * 16 + 64) == B.PAB_INVALID_ARG                # workspace not 256-aligned
+    assert bwd(lse=null) == B.PAB_INVALID_ARG
+    assert bwd(dt=7) == B.PAB_INVALID_ARG                             # unknown dO dtype
+    assert bwd(gstr=B._i64([2 * 256 * 128, 256 * 128, 130, 1])) == B.PAB_INVALID_ARG
+    assert bwd(dt=B.PAB_BF16, dstr=B._i64([2 * 256 * 128, 256 * 128, 132, 1])) == B.PAB_INVALID_ARG
+    assert bwd(q=mk(0, d=64), k=mk(0, d=64), v=mk(1, d=64)) == B.PAB_UNSUPPORTED
+    assert bwd(k=mk(2)) == B.PAB_INVALID_ARG                          # mixed Q/K recipes
+    assert bwd(q=mk(0, op=0)) == B.PAB_INVALID_ARG                    # FP8 Q without operand copy
     assert L.pab_last_hip_error() == 0
 
 
