@@ -41,9 +41,10 @@ DEFAULT_CONFIG = "dense_mxfp4_16k"
 PEAK_FP8 = 5000.0
 PEAK_FP4 = 10100.0
 PEAK_BF16 = 2500.0
+PEAK_BF16 = 2500.0
 # sources that define the attention kernel's code; a counter summary is valid
 # only for the sources it was taken on
-KERNEL_SOURCES = ("attention.hip", "pab_device.h", "pab_internal.h")
+KERNEL_SOURCES = ("attention.hip", "pab_device.h", "pab_internal.h", "pab_lds.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attention_%s_counters.md")
 
 
@@ -179,6 +180,70 @@ def time_gpu(path, steps, warmup):
     return wall, q_ms, a_ms
 
 
+def time_backward(cfg, path, steps, warmup):
+    """The backward pass (prep kernels, dK/dV, dQ) of the dense or causal
+    workload: one forward with the row statistic, then `steps` timed backward
+    calls on a seeded bf16 dO; returns per-call milliseconds."""
+    import torch
+    lib = path.lib
+    qq, kq, vq = path.quantize()
+    causal = cfg.mode == "causal"
+    out, lse = lib.attention_dense(qq, kq, vq, causal=causal, lse=True)
+    g = torch.Generator(device="cpu").manual_seed(1000 * cfg.index + 7)
+    dout = torch.randn(out.shape, generator=g).to(torch.bfloat16).cuda()
+    ws = torch.empty(lib.backward_workspace_bytes(cfg.B, cfg.H, cfg.n_kernel, cfg.d),
+                     dtype=torch.uint8, device="cuda")
+    grads = tuple(torch.empty_like(out) for _ in range(3))
+    call = lambda: lib.attention_backward(qq, kq, vq, out, dout, lse, causal=causal,
+                                          workspace=ws, grads=grads)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(st)
+        call()
+        e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def backward_main(args, cfg, path):
+    if cfg.mode not in ("dense", "causal") or path.dplan is not None:
+        print("--backward runs the dense and causal workloads (the backward pass has no "
+              "sliding-tile or token-permuted form)", file=sys.stderr)
+        sys.exit(2)
+    print("[bench] timing %d backward steps after %d warm-up" % (args.steps, args.warmup),
+          file=sys.stderr, flush=True)
+    wall, ms = time_backward(cfg, path, args.steps, args.warmup)
+    flops = 2.5 * algorithmic_flops(cfg, None)       # five products of 2 N^2 d (causal: half)
+    ms_call = float(np.mean(ms))
+    achieved = flops / (ms_call * 1e-3) / 1e12
+    result = {
+        "metric": "effective attention backward TFLOPS (10*N^2*d*H: dQ, dK, dV) + % of bf16 "
+                  "MFMA peak, 1 GPU",
+        "value": round(flops / (wall / args.steps) / 1e12, 2),
+        "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16, outlier channels as configured; dO N(0,1) bf16)",
+        "config": {"workload": cfg.name + "_backward", "desc": "backward pass of " + cfg.desc,
+                   "B": cfg.B, "H": cfg.H, "N": cfg.n_real, "d": cfg.d, "mode": cfg.mode,
+                   "recipe": cfg.recipe, "algorithmic_flops": flops,
+                   "backward_ms": round(ms_call, 4),
+                   "backward_ms_min_max": [round(min(ms), 4), round(max(ms), 4)]},
+        "roofline": {"bound": "mfma", "kernel": "whole backward call (prep, dK/dV, dQ)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result))
+
+
 def cpu_baseline(cfg, x, plan, bn, budget_s=15.0):
     """The oracle (as it stands) on a bounded sample: quantise one head's Q, K,
     V and run the recipe for a set of query rows of that head; scaled to the
@@ -252,6 +317,9 @@ def main():
     ap.add_argument("--tau", type=int, default=0,
                     help="softmax rescale threshold in log2 units (0 = rescale on every rise of "
                          "the running maximum, the default recipe)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dQ, dK, dV) of a dense or causal workload "
+                         "instead of the forward step")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device copy of this many bytes "
                          "(counter calibration for rocprofv3 --pmc runs)")
@@ -271,6 +339,9 @@ def main():
     print("[bench] config %s: generating inputs" % cfg.name, file=sys.stderr, flush=True)
     x = make_inputs(cfg, as_torch=True)
     path = GpuPath(cfg, x, lib, args.tau)
+    if args.backward:
+        backward_main(args, cfg, path)
+        return
     mode = {"dense": 0, "causal": 1, "sta": 2}[cfg.mode]
     _, bn = lib.attention_info("fp8_block" if cfg.recipe == "fp8" else "mxfp4", cfg.d, mode)
     print("[bench] timing %d steps after %d warm-up" % (args.steps, args.warmup), file=sys.stderr,

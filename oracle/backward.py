@@ -76,3 +76,38 @@ def attention_backward(q, k, v, o, do, lse, *, sm_scale, causal=False, kv_valid=
     if kv_valid is not None:
         mask &= np.asarray(kv_valid, dtype=bool)[None, :]
     return backward_core(qh, kh, vh, o, do, lse, sm_scale, mask)
+
+
+def backward_sampled(qh, kh, vh, o, do, lse, sm_scale, rows, cols, causal=False, kv_valid=None):
+    """The same gradients evaluated only where they are sampled: dQ for the
+    query rows `rows` and dK, dV for the keys `cols` (float64), from
+    dequantised operands [N, d], the forward output o and lse of every row
+    and the upstream gradient do [N, d].  Each sampled row (key) uses all keys
+    (queries), so the cost is linear in N per sample."""
+    qh, kh, vh, o, do = (np.asarray(a, dtype=np.float64) for a in (qh, kh, vh, o, do))
+    lse = np.asarray(lse, dtype=np.float64)
+    rows, cols = np.asarray(rows, np.int64), np.asarray(cols, np.int64)
+    n = qh.shape[0]
+    kvalid = np.ones(n, bool) if kv_valid is None else np.asarray(kv_valid, bool)
+    ok = np.isfinite(lse)
+    dd = (do * o).sum(axis=1)
+
+    def probs(s, ri, ci):
+        m = ok[ri][:, None] & kvalid[ci][None, :]
+        if causal:
+            m &= ci[None, :] <= ri[:, None]
+        with np.errstate(invalid="ignore", over="ignore"):
+            p = np.exp2(s - np.where(ok[ri], lse[ri], 0.0)[:, None])
+        return np.where(m, p, 0.0)
+
+    allq = np.arange(n)
+    # rows: dQ_i = sm sum_j P_ij (dP_ij - D_i) K^_j
+    p = probs((qh[rows] @ kh.T) * (sm_scale * LOG2E), rows, allq)
+    ds = p * (do[rows] @ vh.T - dd[rows][:, None])
+    dq = sm_scale * (ds @ kh)
+    # keys: dK_j = sm sum_i dS_ij Q^_i, dV_j = sum_i P_ij dO_i
+    p = probs((qh @ kh[cols].T) * (sm_scale * LOG2E), allq, cols)
+    ds = p * (do @ vh[cols].T - dd[:, None])
+    dk = sm_scale * (ds.T @ qh)
+    dv = p.T @ do
+    return dq, dk, dv

@@ -89,3 +89,55 @@ def head_job(job):
         out[:] = OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm, bn=bn,
                                      causal=cfg.mode == "causal", kv_valid=kv_valid)
     return head, tokens, out, digests
+
+
+U_BF16 = 2.0 ** -8
+
+
+def head_backward_job(job):
+    """Backward pass of one head at full size: (config name, shm names of q,
+    k, v, dO, shape, head, query rows, keys, bn) -> (head, O [N, d] float32,
+    LSE [N] float32, dQ[rows], dK[keys], dV[keys], and the first-order bounds
+    of the library's bf16 roundings for those elements).  The oracle forward
+    runs for every row (the keys' gradients need all of them)."""
+    from oracle import backward as OB
+    name, shm_names, shape, head, rows, cols, bn = job
+    cfg = CONFIGS[name]
+    blocks = [shared_memory.SharedMemory(name=n) for n in shm_names]
+    try:
+        q, k, v, do = (np.ndarray(shape, np.float32, buffer=b.buf)[0, head].copy() for b in blocks)
+    finally:
+        for b in blocks:
+            b.close()
+    qc, qs = OQ.fp8_block_quantize(q, cfg.blk)
+    kc, ks = OQ.fp8_block_quantize(k, cfg.blk)
+    vc, vs = OQ.fp8_channel_quantize(v)
+    qo, ko = OA.Operand("fp8_block", qc, qs, cfg.blk), OA.Operand("fp8_block", kc, ks, cfg.blk)
+    vo = OA.Operand("fp8_channel", vc, vs)
+    n = q.shape[0]
+    sm = 1.0 / np.sqrt(cfg.d)
+    causal = cfg.mode == "causal"
+    o, lse = OA.recipe_attention(qo, ko, vo, np.arange(n), sm_scale=sm, bn=bn, causal=causal,
+                                 return_lse=True)
+    qh, kh, vh = OB.dequantized(qo), OB.dequantized(ko), OB.dequantized(vo)
+    do = do.astype(np.float64)
+    grads = OB.backward_sampled(qh, kh, vh, o, do, lse, sm, rows, cols, causal=causal)
+    # bounds: sm u (P A + |dS|) |K^| for dQ rows, its transpose with |Q^| for dK,
+    # 2 u P^T |dO| for dV (A = |dO| |V^|^T)
+    l64 = lse.astype(np.float64)
+    dd = (do * o).sum(axis=1)
+    allq = np.arange(n)
+
+    def pmat(ri, ci):
+        s = (qh[ri] @ kh[ci].T) * (sm * OA.LOG2E)
+        p = np.exp2(s - l64[ri][:, None])
+        return np.where(ci[None, :] <= ri[:, None], p, 0.0) if causal else p
+
+    p = pmat(rows, allq)
+    w = p * (np.abs(do[rows]) @ np.abs(vh).T) + np.abs(p * (do[rows] @ vh.T - dd[rows][:, None]))
+    bq = sm * U_BF16 * (w @ np.abs(kh))
+    p = pmat(allq, cols)
+    w = p * (np.abs(do) @ np.abs(vh[cols]).T) + np.abs(p * (do @ vh[cols].T - dd[:, None]))
+    bk = sm * U_BF16 * (w.T @ np.abs(qh))
+    bv = 2 * U_BF16 * (p.T @ np.abs(do))
+    return head, o, lse, grads, (bq, bk, bv)

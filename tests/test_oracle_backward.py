@@ -164,3 +164,20 @@ def test_forward_lse_is_the_log2_sum_of_exponentials(tau):
     _, lse_m = A.recipe_attention(qo, ko, vo, np.arange(4), sm_scale=sm, bn=64,
                                   kv_valid=np.zeros(n, np.uint8), return_lse=True)
     assert np.all(np.isneginf(lse_m))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_gradients_equal_the_full_ones(causal):
+    n, d = 70, 16
+    q, k, v, do = _tiny(n, d, 36)
+    valid = np.ones(n, bool)
+    valid[[5, 44]] = False
+    mask = valid[None, :] & (np.tri(n, dtype=bool) if causal else True)
+    o, lse = _fwd(q, k, v, 0.4, mask)
+    full = G.backward_core(q, k, v, o, do, lse, 0.4, mask)
+    rows, cols = np.array([0, 3, 44, 69]), np.array([0, 5, 17, 69])
+    dq, dk, dv = G.backward_sampled(q, k, v, o, do, lse, 0.4, rows, cols, causal=causal,
+                                    kv_valid=valid)
+    assert np.allclose(dq, full[0][rows], rtol=1e-12, atol=1e-14)
+    assert np.allclose(dk, full[1][cols], rtol=1e-12, atol=1e-14)
+    assert np.allclose(dv, full[2][cols], rtol=1e-12, atol=1e-14)
