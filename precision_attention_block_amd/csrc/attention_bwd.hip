@@ -31,6 +31,8 @@
 // so the scores never leave the registers.
 // Tiles reach LDS by LDS-DMA into XOR-swizzled rows (conflict-free 16-byte
 // operand reads), one step ahead of the step being computed.
+#include <type_traits>
+
 #include "pab_bwd.h"
 #include "pab_device.h"
 #include "pab_lds.h"
@@ -79,18 +81,21 @@ __device__ inline float e2m1_value(uint32_t nib) {
 }
 
 // Writes the transposed copy of a 64-token x 128-channel bf16 tile (row pitch
-// TP elements) to dst[c * n_alloc + slot], slots in swap23 order.
+// TP elements) in the block-tiled layout [token block of 32][channel][32
+// slots], slots in swap23 order: dst points at the tile's first block.  One
+// 32-token step of a transposed operand is then 8 contiguous KB.
 template <int TP>
-__device__ inline void store_transposed(const uint16_t* tile, uint16_t* dst, int n_alloc, int tid) {
+__device__ inline void store_transposed(const uint16_t* tile, uint16_t* dst, int tid) {
   for (int u = tid; u < kD * 8; u += 256) {
-    const int c = u / 8, ch = u % 8;
+    const int c = u / 8, ch = u % 8;   // channel, 8-slot chunk of the 64 tokens
     uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s0 = 8 * ch + 2 * j;
       w[j] = (uint32_t)tile[swap23(s0) * TP + c] | ((uint32_t)tile[swap23(s0 + 1) * TP + c] << 16);
     }
-    *reinterpret_cast<uint4*>(dst + (int64_t)c * n_alloc + 8 * ch) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(dst + (ch / 4) * kD * 32 + c * 32 + 8 * (ch % 4)) =
+        make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(256) void bwd_prep_qk_kernel(BwdArgs a) {
     (isk ? a.fk : a.fq)[tokb + tid] = f;
   }
   __syncthreads();
-  store_transposed<TP>(tile, (isk ? a.kt : a.qt) + (int64_t)bh * kD * a.n_alloc + t0, a.n_alloc, tid);
+  store_transposed<TP>(tile, (isk ? a.kt : a.qt) + ((int64_t)bh * a.n_alloc + t0) * kD, tid);
 }
 
 // ---- prep: V values as bf16 rows ---------------------------------------------
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(256) void bwd_prep_do_kernel(BwdArgs a) {
     if (bh == 0) a.kvf[tok] = (live && (!a.kv_valid || a.kv_valid[tok])) ? 1.0f : 0.0f;
   }
   __syncthreads();
-  store_transposed<TP>(tile, a.dot + (int64_t)bh * kD * a.n_alloc + t0, a.n_alloc, tid);
+  store_transposed<TP>(tile, a.dot + ((int64_t)bh * a.n_alloc + t0) * kD, tid);
 }
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -260,9 +265,10 @@ __device__ inline v8s lds_t_operand(const uint8_t* base, int row, int chunk) {
 }
 
 // Copies of one step: 8 KB row tiles take 8 instructions of 1 KB (4 rows),
-// 8 KB transposed tiles 8 instructions (16 rows); each wave issues 2 of each
-// tile's 8.  The per-token floats are one full-wave dword copy each, issued
-// by every wave to the same place.
+// 8 KB transposed tiles 8 instructions (16 rows of 64 bytes, contiguous in
+// the block-tiled layout); each wave issues 2 of each tile's 8.  The
+// per-token floats are one full-wave dword copy each, issued by every wave to
+// the same place.
 __device__ inline void issue_rows(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int t0, int wave,
                                   const DmaPlan<16>& pr) {
 #pragma unroll
@@ -272,13 +278,13 @@ __device__ inline void issue_rows(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int t0
                                              (t0 + 4 * inst) * 2 * kD, 0, 0);
   }
 }
-__device__ inline void issue_trans(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int t0, int n_alloc,
-                                   int wave, const DmaPlan<4>& pt) {
+__device__ inline void issue_trans(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int t0, int wave,
+                                   const DmaPlan<4>& pt) {
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int inst = 2 * wave + x;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + inst * 1024), 16, pt.off[0],
-                                             t0 * 2 + inst * 16 * 2 * n_alloc, 0, 0);
+                                             t0 * 2 * kD + inst * 1024, 0, 0);
   }
 }
 __device__ inline void issue_floats(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int t0, int lane) {
@@ -298,10 +304,13 @@ __device__ inline v8s pack_b(const float (&x)[16], int h) {
 #endif  // __HIP_DEVICE_COMPILE__
 
 // ---- dK, dV --------------------------------------------------------------------
-template <bool CAUSAL>
+// UQ: the Q block scale is the same for all 32 queries of a step (MXFP4, or
+// FP8 blocks of a multiple of 32 tokens), so one fma forms each exponent
+// argument and dS takes one fma and one multiply.
+template <bool CAUSAL, bool UQ>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __align__(16) uint8_t st0[Stage::BYTES], st1[Stage::BYTES];
+  __shared__ __align__(16) uint8_t st0[Stage::BYTES], st1[Stage::BYTES], st2[Stage::BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
@@ -337,12 +346,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   DmaPlan<16> pr;
   pr.init(lane, 2 * kD);
   DmaPlan<4> pt;
-  pt.init(lane, 2 * (int64_t)a.n_alloc);
+  pt.init(lane, 64);   // transposed rows of one step are 64 bytes apart
   auto issue = [&](uint8_t* stg, int q0) __attribute__((always_inline)) {
     issue_rows(qr, stg + Stage::R0, q0, wave, pr);
     issue_rows(dr, stg + Stage::R1, q0, wave, pr);
-    issue_trans(qtr, stg + Stage::T0, q0, a.n_alloc, wave, pt);
-    issue_trans(dtr, stg + Stage::T1, q0, a.n_alloc, wave, pt);
+    issue_trans(qtr, stg + Stage::T0, q0, wave, pt);
+    issue_trans(dtr, stg + Stage::T1, q0, wave, pt);
     issue_floats(lsr, stg + Stage::F0, q0, lane);
     issue_floats(ddr, stg + Stage::F1, q0, lane);
     issue_floats(fqr, stg + Stage::F2, q0, lane);
@@ -354,19 +363,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) dvt[cb][e] = dkt[cb][e] = 0.0f;
 
-  const int q_begin = CAUSAL ? kt * kBwdTile : 0;   // earlier queries see none of these keys
-  const int q_end = (a.N + 31) / 32 * 32;
-  issue(st0, q_begin);
-  int it = 0;
-  for (int q0 = q_begin; q0 < q_end; q0 += 32, ++it) {
-    const uint8_t* cur = (it & 1) ? st1 : st0;
-    wait_vm_le<0>();
-    barrier_lds();   // this step has landed everywhere; every wave is done with the other stage
-    if (q0 + 32 < q_end) issue((it & 1) ? st0 : st1, q0 + 32);
-    if (CAUSAL && q0 + 32 <= key0) continue;   // every query of the step precedes this wave's keys
-
-    // S (queries x keys) = Q K^T and dP = (dO / s_V) V_codes^T
-    v16f s, dp;
+  // S (queries x keys) = Q K^T and dP = (dO / s_V) V_codes^T of the step in
+  // stage `cur`.  Register 4 i + r of the score tiles is query q0 + 8 i +
+  // 4 lg + r.
+  auto products = [&](const uint8_t* cur, v16f& s, v16f& dp) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
 #pragma unroll
@@ -376,44 +376,104 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R1, lr, 2 * ks + lg), vb[ks],
                                                    dp, 0, 0, 0);
     }
-    // register 4 i + r is query q0 + 8 i + 4 lg + r
-    float4 ls4[4], dd4[4], fq4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ls4[i] = *reinterpret_cast<const float4*>(cur + Stage::F0 + 4 * (8 * i + 4 * lg));
-      dd4[i] = *reinterpret_cast<const float4*>(cur + Stage::F1 + 4 * (8 * i + 4 * lg));
-      fq4[i] = *reinterpret_cast<const float4*>(cur + Stage::F2 + 4 * (8 * i + 4 * lg));
+  };
+  // The rest of a step from its scores: P, dS and the dV / dK products.
+  auto finish = [&](const int q0, const uint8_t* cur, const v16f& s, const v16f& dp)
+      __attribute__((always_inline)) {
+    float cs = 0.0f, sc = 0.0f;
+    if (UQ) {
+      const float fq = *reinterpret_cast<const float*>(cur + Stage::F2);
+      cs = ck * fq;        // exponent argument: S cs - LSE
+      sc = a.sm * fq;      // dS scaled for dK^ = sm dS^T Q^
     }
     const bool masked = !all_valid || (CAUSAL && q0 < key0 + 32);
-    float p[16], ds[16];
+    // P = 2^(S c - LSE), dS' = P (dP - D) sm / s_Q, packed per half h into
+    // the bf16 B operands of the products over queries 16 h .. 16 h + 15.
+    // Masked steps keep register 4 i + r only if 8 i + r >= thr (query >= key
+    // for causal masks; never for a masked key).
+    const int thr = !kvalid ? 64 : CAUSAL ? j - q0 - 4 * lg : -64;
+    v8s pb[2], db[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int i = e / 4, r = e % 4;
-      const float lse = r == 0 ? ls4[i].x : r == 1 ? ls4[i].y : r == 2 ? ls4[i].z : ls4[i].w;
-      const float dd = r == 0 ? dd4[i].x : r == 1 ? dd4[i].y : r == 2 ? dd4[i].z : dd4[i].w;
-      const float fq = r == 0 ? fq4[i].x : r == 1 ? fq4[i].y : r == 2 ? fq4[i].z : fq4[i].w;
-      float pe = __builtin_amdgcn_exp2f(fmaf(s[e] * ck, fq, -lse));
-      if (masked) {
-        const int q = q0 + 8 * i + 4 * lg + r;
-        pe = (kvalid && (!CAUSAL || q >= j)) ? pe : 0.0f;
+    for (int h = 0; h < 2; ++h) {
+      float p[8], ds[8];
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * h + ii;
+        const float4 l4 = *reinterpret_cast<const float4*>(cur + Stage::F0 + 4 * (8 * i + 4 * lg));
+        const float4 d4 = *reinterpret_cast<const float4*>(cur + Stage::F1 + 4 * (8 * i + 4 * lg));
+        float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (!UQ) f4 = *reinterpret_cast<const float4*>(cur + Stage::F2 + 4 * (8 * i + 4 * lg));
+        const float lse[4] = {l4.x, l4.y, l4.z, l4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float fq[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * i + r;
+          const float pe = __builtin_amdgcn_exp2f(UQ ? fmaf(s[e], cs, -lse[r]) : fmaf(s[e] * ck, fq[r], -lse[r]));
+          p[4 * ii + r] = pe;
+          ds[4 * ii + r] = UQ ? pe * fmaf(dp[e], sc, -dd[r] * sc) : pe * (dp[e] - dd[r]) * (a.sm * fq[r]);
+        }
       }
-      p[e] = pe;
-      ds[e] = pe * (dp[e] - dd) * (a.sm * fq);   // dS scaled for dK^ = sm dS^T Q^
+      if (masked) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const bool keep = 8 * (2 * h + x / 4) + x % 4 >= thr;
+          p[x] = keep ? p[x] : 0.0f;
+          ds[x] = keep ? ds[x] : 0.0f;
+        }
+      }
+      pb[h] = __builtin_bit_cast(v8s, make_uint4(bf16x2(p[0], p[1]), bf16x2(p[2], p[3]),
+                                                 bf16x2(p[4], p[5]), bf16x2(p[6], p[7])));
+      db[h] = __builtin_bit_cast(v8s, make_uint4(bf16x2(ds[0], ds[1]), bf16x2(ds[2], ds[3]),
+                                                 bf16x2(ds[4], ds[5]), bf16x2(ds[6], ds[7])));
     }
     // dV^T += dO^T P and dK^T += Q_vals^T dS' (channels x keys, K = queries)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const v8s pb = pack_b(p, h), dsb = pack_b(ds, h);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const int row = 32 * cb + lr;
-        dvt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T1, row, 2 * h + lg), pb,
+        dvt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T1, row, 2 * h + lg), pb[h],
                                                           dvt[cb], 0, 0, 0);
-        dkt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T0, row, 2 * h + lg), dsb,
+        dkt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T0, row, 2 * h + lg), db[h],
                                                           dkt[cb], 0, 0, 0);
       }
-    }
+  };
+
+  const int q_begin = CAUSAL ? kt * kBwdTile : 0;   // earlier queries see none of these keys
+  const int q_end = (a.N + 31) / 32 * 32;
+  // Steps wholly above the diagonal (causal) are computed and masked rather
+  // than skipped: a branch around the products makes the compiler move every
+  // accumulator between register files on each step, and such steps are at
+  // most three per workgroup.
+  // Software pipeline over 32-query steps t (three LDS stages): iteration t
+  // copies step t+2, forms the scores of step t+1 while the vector unit works
+  // on step t, then adds step t's products.  The body has no branch, so the
+  // compiler can interleave the matrix and vector work; past the last step
+  // the copies and score products run on data that is never used (the
+  // buffer descriptors bound every copy).
+  const int n_steps = (q_end - q_begin) / 32;
+  auto stage = [&](int i) __attribute__((always_inline)) { return i == 0 ? st0 : i == 1 ? st1 : st2; };
+  issue(st0, q_begin);
+  issue(st1, q_begin + 32);
+  constexpr int kIssues = 11;   // copy instructions per wave per stage
+  wait_vm_le<kIssues>();
+  barrier_lds();
+  v16f sa, dpa, sb, dpb;
+  products(st0, sa, dpa);
+  auto body = [&](const int t, v16f& s_cur, v16f& dp_cur, v16f& s_nxt, v16f& dp_nxt)
+      __attribute__((always_inline)) {
+    wait_vm_le<0>();
+    barrier_lds();   // step t+1 has landed everywhere; stage (t+2) % 3 is free
+    issue(stage((t + 2) % 3), q_begin + 32 * (t + 2));
+    products(stage((t + 1) % 3), s_nxt, dp_nxt);
+    finish(q_begin + 32 * t, stage(t % 3), s_cur, dp_cur);
+  };
+  int t = 0;
+  for (; t + 2 <= n_steps; t += 2) {
+    body(t, sa, dpa, sb, dpb);
+    body(t + 1, sb, dpb, sa, dpa);
   }
+  if (t < n_steps) finish(q_begin + 32 * t, stage(t % 3), sa, dpa);   // odd count: the last step
   wait_vm_le<0>();   // no copy may still target this workgroup's LDS when it ends
   // lane (key j, lg) holds channels 32 cb + 8 i + 4 lg + r
   if (j < a.N) {
@@ -473,11 +533,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   DmaPlan<16> pr;
   pr.init(lane, 2 * kD);
   DmaPlan<4> pt;
-  pt.init(lane, 2 * (int64_t)a.n_alloc);
+  pt.init(lane, 64);   // transposed rows of one step are 64 bytes apart
   auto issue = [&](uint8_t* stg, int k0) __attribute__((always_inline)) {
     issue_rows(kr, stg + Stage::R0, k0, wave, pr);
     issue_rows(vr, stg + Stage::R1, k0, wave, pr);
-    issue_trans(ktr, stg + Stage::T0, k0, a.n_alloc, wave, pt);
+    issue_trans(ktr, stg + Stage::T0, k0, wave, pt);
     issue_floats(fkr, stg + Stage::F0, k0, lane);
     issue_floats(kvr, stg + Stage::F1, k0, lane);
   };
@@ -572,11 +632,19 @@ hipError_t launch_attention_backward(const BwdArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL(bwd_prep_do_kernel<float>, g64, dim3(256), 0, st, a);
   const dim3 gt(BH * (unsigned)(a.n_alloc / kBwdTile));
+  // the Q scale is uniform over 32-query steps for MXFP4 (1) and for FP8 blocks of 32k tokens
+  const bool uq = a.qk_mx || a.blk_q % 32 == 0;
   if (a.causal) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, gt, dim3(256), 0, st, a);
+    if (uq)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<true, true>), gt, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<true, false>), gt, dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_dq_kernel<true>, gt, dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, gt, dim3(256), 0, st, a);
+    if (uq)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<false, true>), gt, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<false, false>), gt, dim3(256), 0, st, a);
     hipLaunchKernelGGL(bwd_dq_kernel<false>, gt, dim3(256), 0, st, a);
   }
   return hipGetLastError();

@@ -8,9 +8,9 @@ namespace pab {
 
 // Device arrays of the backward pass.  Token arrays have n_alloc slots per
 // (batch, head); "rows" are [BH][n_alloc][d] bf16, "transposed" arrays are
-// [BH][d][n_alloc] bf16 with, inside every 16-token group, token t at slot t
-// with bits 2 and 3 swapped (the K order in which a 32x32 MFMA result lane
-// holds its 16 values, see attention_bwd.hip).
+// block-tiled [BH][n_alloc/32][d][32] bf16 with, inside every 16-token group,
+// token t at slot t with bits 2 and 3 swapped (the K order in which a 32x32
+// MFMA result lane holds its 16 values, see attention_bwd.hip).
 struct BwdArgs {
   int B, H, N, n_alloc, d;
   float sm;                    // sm_scale
