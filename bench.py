@@ -152,7 +152,7 @@ class GpuPath:
         if self.dplan is not None:
             return lib.attention_dense(qq, kq, vq, kv_valid=self.dplan.kv_valid,
                                        out_perm=self.dplan.perm, n_out=cfg.n_real, out=self.out,
-                                       tau=self.tau)
+                                       tau=self.tau, key_tiles=self.dplan.key_tiles)
         return lib.attention_dense(qq, kq, vq, causal=cfg.mode == "causal", out=self.out,
                                    tau=self.tau)
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define PAB_ABI_VERSION 3
+#define PAB_ABI_VERSION 4
 #define PAB_TOKEN_ALIGN 128  /* query tile of the attention kernel */
 #define PAB_MAX_TAU 8        /* largest softmax rescale threshold (log2 units) */
 
@@ -91,7 +91,7 @@ int64_t pab_token_alloc(int64_t n);
  * tiles of BN keys in ascending order and requantises P against the running
  * maximum including the current tile, so BN is part of the result's
  * definition (the reference oracle takes it as a parameter).
- * mode: 0 dense, 1 causal, 2 sliding-tile. */
+ * mode: 0 dense, 1 causal, 2 sliding-tile, 3 dense over listed key tiles. */
 pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, int* BN);
 
 /*
@@ -194,6 +194,32 @@ pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab
                                int causal, float sm_scale, int tau, const uint8_t* kv_valid,
                                const int32_t* out_perm, int64_t n_out_tokens, float* out,
                                const int64_t out_strides[4], float* lse, void* stream);
+
+/*
+ * pab_attention_dense_tiles - pab_attention_dense without a causal mask that
+ * visits only the BN-key tiles listed in key_tiles (tile t = keys t*BN ..
+ * t*BN+BN-1; BN from pab_attention_info): a padded sequence skips the tiles
+ * that hold no valid key.  key_tiles is a device int32 array of n_key_tiles
+ * ascending tile indices.  Every key outside the listed tiles must be masked
+ * by kv_valid (required here); the result then equals pab_attention_dense
+ * with the same kv_valid bit for bit, since a tile without a valid key leaves
+ * the online softmax unchanged.  pab_key_tiles builds the list.  Query tiles
+ * whose queries out_perm maps nowhere are skipped when lse is NULL.
+ */
+pab_status pab_attention_dense_tiles(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                     float sm_scale, int tau, const int32_t* key_tiles,
+                                     int n_key_tiles, const uint8_t* kv_valid,
+                                     const int32_t* out_perm, int64_t n_out_tokens, float* out,
+                                     const int64_t out_strides[4], float* lse, void* stream);
+
+/*
+ * pab_key_tiles - host helper: the indices of the BN-key tiles of kv_valid
+ * (host uint8 [n]) that hold at least one nonzero entry, ascending, into
+ * tiles (host int32, may be NULL to count only); *count receives their
+ * number.  bn must be the kernel's BN (pab_attention_info).
+ */
+pab_status pab_key_tiles(const uint8_t* kv_valid, int64_t n, int bn, int32_t* tiles,
+                         int64_t* count);
 
 /*
  * pab_attention_sta - sliding-tile sparse attention [FPS §2.2]: the N tokens

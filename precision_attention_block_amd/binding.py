@@ -22,7 +22,7 @@ EXPORTS = [
     "pab_abi_version", "pab_status_str", "pab_last_hip_error", "pab_token_alloc",
     "pab_attention_info", "pab_quantize", "pab_attention_dense", "pab_attention_sta",
     "pab_sta_plan", "pab_count_nonfinite", "pab_attention_backward_workspace",
-    "pab_attention_backward",
+    "pab_attention_backward", "pab_attention_dense_tiles", "pab_key_tiles",
 ]
 
 
@@ -74,6 +74,11 @@ def _lib():
         L.pab_attention_sta.argtypes = [ctypes.POINTER(QView)] * 3 + [
             ctypes.c_float, ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp,
             ctypes.c_int64, vp, i64p, vp, vp]
+        L.pab_attention_dense_tiles.restype = ctypes.c_int
+        L.pab_attention_dense_tiles.argtypes = [ctypes.POINTER(QView)] * 3 + [
+            ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp, i64p, vp, vp]
+        L.pab_key_tiles.restype = ctypes.c_int
+        L.pab_key_tiles.argtypes = [vp, ctypes.c_int64, ctypes.c_int, vp, i64p]
         L.pab_attention_backward_workspace.restype = ctypes.c_int64
         L.pab_attention_backward_workspace.argtypes = [ctypes.c_int64] * 4
         L.pab_attention_backward.restype = ctypes.c_int
@@ -195,15 +200,43 @@ def _lse_tensor(q, lse):
     return lse or None
 
 
+def key_tiles(kv_valid_host):
+    """Ascending indices (int32 numpy) of the key tiles of kv_valid (host uint8
+    numpy) that hold a valid key (pab_key_tiles)."""
+    kv = np.ascontiguousarray(kv_valid_host, dtype=np.uint8)
+    bn = attention_info("fp8_block", 128, 0)[1]
+    cnt = ctypes.c_int64()
+    _check(_lib().pab_key_tiles(kv.ctypes.data, kv.size, bn, None, ctypes.byref(cnt)), "pab_key_tiles")
+    out = np.zeros(max(cnt.value, 1), np.int32)
+    _check(_lib().pab_key_tiles(kv.ctypes.data, kv.size, bn, out.ctypes.data, ctypes.byref(cnt)),
+           "pab_key_tiles")
+    return out[:cnt.value]
+
+
 def attention_dense(q, k, v, causal=False, sm_scale=None, kv_valid=None, out_perm=None,
-                    n_out=None, out=None, tau=0, lse=None):
+                    n_out=None, out=None, tau=0, lse=None, key_tiles=None):
     """O = softmax(Q K^T sm_scale) V on quantised operands; returns float32
     [B, H, n_out, d] (n_out defaults to N).  tau: softmax rescale threshold
     (see pab_attention_dense).  lse: None, True (allocate) or a float32
-    [B, H, N] tensor for the row statistic; when given, returns (O, lse)."""
+    [B, H, N] tensor for the row statistic; when given, returns (O, lse).
+    key_tiles: int32 device tensor of the key tiles to visit (non-causal, with
+    kv_valid masking every other key; pab_attention_dense_tiles)."""
     n_out = q.N if n_out is None else int(n_out)
     out = _out_tensor(q, n_out, out)
     lse_t = _lse_tensor(q, lse)
+    if key_tiles is not None:
+        if causal or kv_valid is None:
+            raise ValueError("key_tiles needs a non-causal call with kv_valid")
+        qv, kv, vv = q.view(), k.view(), v.view()
+        st = _lib().pab_attention_dense_tiles(
+            ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(sm_scale or 0.0), int(tau),
+            ctypes.c_void_p(key_tiles.data_ptr()), int(key_tiles.numel()),
+            ctypes.c_void_p(kv_valid.data_ptr()),
+            ctypes.c_void_p(out_perm.data_ptr() if out_perm is not None else 0), n_out,
+            ctypes.c_void_p(out.data_ptr()), _i64(out.stride()),
+            ctypes.c_void_p(lse_t.data_ptr() if lse_t is not None else 0), _stream(out.device))
+        _check(st, "pab_attention_dense_tiles")
+        return (out, lse_t) if lse_t is not None else out
     qv, kv, vv = q.view(), k.view(), v.view()
     st = _lib().pab_attention_dense(
         ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), int(bool(causal)),
@@ -310,6 +343,8 @@ class DevicePlan:
         import torch
         for name in ("perm", "inv_perm", "kv_valid", "win_off", "win_idx", "lpt"):
             setattr(self, name, torch.from_numpy(getattr(hp, name)).to(device))
+        # key tiles holding a valid key, for dense attention on the padded grid
+        self.key_tiles = torch.from_numpy(key_tiles(hp.kv_valid)).to(device)
         self.n_tokens, self.n_tiles, self.n_pairs = hp.n_tokens, hp.n_tiles, hp.n_pairs
         self.tile_tokens, self.n_real = hp.tile_tokens, hp.n_real
 

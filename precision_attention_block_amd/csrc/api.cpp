@@ -146,7 +146,7 @@ int64_t pab_token_alloc(int64_t n) { return n <= 0 ? 0 : round_up(n, PAB_TOKEN_A
 
 pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, int* BN) {
   if (!BM || !BN) return PAB_INVALID_ARG;
-  if (mode < 0 || mode > 2) return PAB_INVALID_ARG;
+  if (mode < 0 || mode > 3) return PAB_INVALID_ARG;
   if (qk_recipe == PAB_FP8_TOKEN_BLOCK) {
     if (d != 64 && d != 128) return PAB_UNSUPPORTED;
   } else if (qk_recipe == PAB_MXFP4_D32) {
@@ -155,7 +155,8 @@ pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, in
     return PAB_INVALID_ARG;
   }
   // dense FP8 attention with d = 128 runs the 8-wave kernel (256 queries)
-  *BM = (qk_recipe == PAB_FP8_TOKEN_BLOCK && d == 128 && mode == 0) ? 2 * pab::kBM : pab::kBM;
+  *BM = (qk_recipe == PAB_FP8_TOKEN_BLOCK && d == 128 && (mode == 0 || mode == 3)) ? 2 * pab::kBM
+                                                                                 : pab::kBM;
   *BN = pab::kBN;
   return PAB_OK;
 }
@@ -230,6 +231,46 @@ pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab
   return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32,
                                           v->recipe == PAB_MXFP4_V, causal ? 1 : 0, st),
                     st);
+}
+
+pab_status pab_attention_dense_tiles(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                     float sm_scale, int tau, const int32_t* key_tiles,
+                                     int n_key_tiles, const uint8_t* kv_valid,
+                                     const int32_t* out_perm, int64_t n_out_tokens, float* out,
+                                     const int64_t out_strides[4], float* lse, void* stream) {
+  if (!key_tiles || !kv_valid || !aligned(key_tiles, 4)) return PAB_INVALID_ARG;
+  pab::AttnArgs a;
+  pab_status s = fill_attn_args(q, k, v, sm_scale, tau, kv_valid, out_perm, n_out_tokens, out,
+                                out_strides, a);
+  if (s != PAB_OK) return s;
+  if (n_key_tiles < 1 || (int64_t)n_key_tiles * pab::kBN > round_up(q->N, pab::kBN))
+    return PAB_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return PAB_INVALID_ARG;
+  a.lse = lse;
+  a.key_tiles = key_tiles;
+  a.n_key_tiles = n_key_tiles;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32,
+                                          v->recipe == PAB_MXFP4_V, 3, st),
+                    st);
+}
+
+pab_status pab_key_tiles(const uint8_t* kv_valid, int64_t n, int bn, int32_t* tiles,
+                         int64_t* count) {
+  if (!kv_valid || !count || n < 1 || bn != pab::kBN || n > ((int64_t)1 << 28))
+    return PAB_INVALID_ARG;
+  int64_t c = 0;
+  for (int64_t t = 0; t * bn < n; ++t) {
+    const int64_t e = std::min<int64_t>(n, (t + 1) * bn);
+    bool any = false;
+    for (int64_t j = t * bn; j < e && !any; ++j) any = kv_valid[j] != 0;
+    if (any) {
+      if (tiles) tiles[c] = (int32_t)t;
+      ++c;
+    }
+  }
+  *count = c;
+  return PAB_OK;
 }
 
 pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_qview* v,

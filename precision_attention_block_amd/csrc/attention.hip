@@ -235,7 +235,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     if (MODE == 1) qt = a.n_qtiles - 1 - qt;   // longest query tiles first
     q0 = qt * kBM;
     const int all = (a.N + kBN - 1) / kBN;
-    n_steps = MODE == 1 ? min((q0 + kBM) / kBN, all) : all;
+    n_steps = MODE == 1 ? min((q0 + kBM) / kBN, all) : MODE == 3 ? a.n_key_tiles : all;
+  }
+  // Padding queries are stored nowhere: a workgroup made only of them (and
+  // asked for no row statistic) has nothing to do.  Every wave checks all
+  // 128 queries, so the whole workgroup leaves together, before any copy.
+  if ((MODE == 2 || MODE == 3) && a.out_perm && !a.lse) {
+    const bool mine = (q0 + lane < a.N && a.out_perm[q0 + lane] >= 0) ||
+                      (q0 + 64 + lane < a.N && a.out_perm[q0 + 64 + lane] >= 0);
+    if (!__any(mine)) return;
   }
   const int wq0 = q0 + wave * 32;             // first query of this wave
   const int myq = wq0 + lr;                   // this lane's query
@@ -244,9 +252,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // counter is not the one the tile copies count on (a vector load would make
   // every step wait for the copies issued before it).
   typedef const __attribute__((address_space(4))) int32_t const_i32;
-  const_i32* wlist = MODE == 2 ? (const_i32*)(a.win_idx + a.win_off[u]) : nullptr;
+  const_i32* wlist = MODE == 2 ? (const_i32*)(a.win_idx + a.win_off[u])
+                     : MODE == 3 ? (const_i32*)a.key_tiles : nullptr;
   auto step_start = [&](int t) -> int {
     if (MODE == 2) return wlist[t / spt] * a.tile_tokens + (t % spt) * kBN;
+    if (MODE == 3) return wlist[t] * kBN;
     return t * kBN;
   };
 
@@ -448,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // past the end read zeros or in-bounds bytes of the same head (buffer
   // loads check their range) into stages that are never read; sliding-tile
   // steps repeat the last tile, since the window list ends there.
-  auto tile_at = [&](int t) { return MODE == 2 ? step_start(min(t, n_steps - 1)) : t * kBN; };
+  auto tile_at = [&](int t) { return MODE >= 2 ? step_start(min(t, n_steps - 1)) : t * kBN; };
   issue_k<D, MX>(k0, hb, tile_at(0), wave, lane, kp);
   issue_aux<D, MX>(x0, hb, tile_at(0), lane);
   issue_k<D, MX>(k1, hb, tile_at(1), wave, lane, kp);
@@ -864,7 +874,15 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   if (MODE == 1) qt = n_qt - 1 - qt;   // longest query tiles first
   const int q0 = qt * P::BMW;
   const int all = (a.N + kBN - 1) / kBN;
-  const int n_steps = MODE == 1 ? min((q0 + P::BMW) / kBN, all) : all;
+  const int n_steps = MODE == 1 ? min((q0 + P::BMW) / kBN, all) : MODE == 3 ? a.n_key_tiles : all;
+  // first key of step t: MODE 3 visits the listed key tiles only (past the
+  // last step, the last listed tile again: those copies land in stages that
+  // are never read)
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* klist = MODE == 3 ? (const_i32*)a.key_tiles : nullptr;
+  auto key_at = [&](int t) __attribute__((always_inline)) -> int {
+    return MODE == 3 ? klist[min(t, n_steps - 1)] * kBN : t * kBN;
+  };
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + lr;
   const bool q_live = wq0 < a.n_alloc;      // the wave's 32 queries have token slots
@@ -945,7 +963,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   auto copy_item = [&](const int j, const int t, const int r) __attribute__((always_inline)) {
     constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI, KPER = DmaPlan<TL::K_CPR>::PER;
     uint8_t* kbuf = KS[(r + 3) & 3];
-    const int ks_k = (t + 3) * kBN, ks_a = (t + 2) * kBN;
+    const int ks_k = key_at(t + 3), ks_a = key_at(t + 2);
     if (j < P::KI8) {
       if (MX) {
         if (wave < 4)
@@ -960,7 +978,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
                                                  kp.off[inst % KPER], (ks_k + inst * KRPI) * TL::KROW, 0, 0);
       }
     } else if (j == P::KI8) {
-      pp_issue_v<MX>(VS[(r + 2) & 3], hb, a.n_alloc, (t + 2) * kBN, wave, vp);
+      pp_issue_v<MX>(VS[(r + 2) & 3], hb, a.n_alloc, key_at(t + 2), wave, vp);
     } else if (j == P::KI8 + 1) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.m, (lds_void_t*)XS[(r + 2) & 3], 4, 4 * lane, ks_a, 0, 0);
     } else if (!MX && j == P::KI8 + 2) {
@@ -1067,7 +1085,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   };
   // vector phase t: masks, running max, P~(t), row sums, rescale of O
   auto vphase = [&](const int t, const uint8_t* Ar, v16f (&s)[2], v8i& pk) __attribute__((always_inline)) {
-    const int ks = t * kBN;
+    const int ks = key_at(t);
     const float* Cs = reinterpret_cast<const float*>(Ar + TL::M_BYTES);
     float c[8];
     if (MX) {
@@ -1163,11 +1181,11 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 
   // ---- prologue: K(0..2), V(0..1), side data of tiles 0 and 1; S(0)
 #pragma unroll
-  for (int t = 0; t < 3; ++t) pp_issue_k<MX>(KS[t], hb, t * kBN, wave, lane, kp);
+  for (int t = 0; t < 3; ++t) pp_issue_k<MX>(KS[t], hb, key_at(t), wave, lane, kp);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    pp_issue_v<MX>(VS[t], hb, a.n_alloc, t * kBN, wave, vp);
-    issue_aux<D, MX>(XS[t], hb, t * kBN, lane);
+    pp_issue_v<MX>(VS[t], hb, a.n_alloc, key_at(t), wave, vp);
+    issue_aux<D, MX>(XS[t], hb, key_at(t), lane);
   }
   wait_vm_le<0>();
   barrier_lds();
@@ -1246,6 +1264,7 @@ template <int D, bool MX, bool V4 = false>
 static hipError_t launch_mode(const AttnArgs& a, int mode, hipStream_t st) {
   if (mode == 1) return launch_t<D, MX, 1, V4>(a, st);
   if (mode == 2) return launch_t<D, MX, 2, V4>(a, st);
+  if (mode == 3) return launch_t<D, MX, 3, V4>(a, st);
   return launch_t<D, MX, 0, V4>(a, st);
 }
 
@@ -1261,11 +1280,13 @@ static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, int d, bool mx, bool v4, int mode, hipStream_t st) {
+  // mode 3 (dense over listed key tiles) takes the same kernel as dense
   // dense FP8 with d = 128: the ping-pong kernel (its matrix phase, with QK^T
   // on the bf16 MFMA, is long enough to balance the vector phase; for MXFP4
   // and for causal masks the 4-wave kernel measures faster)
   if (v4) return mx && d == 128 ? launch_mode<128, true, true>(a, mode, st) : hipErrorInvalidValue;
   if (!mx && d == 128 && mode == 0) return launch_pp<false, 0>(a, st);
+  if (!mx && d == 128 && mode == 3) return launch_pp<false, 3>(a, st);
   if (mx) return launch_mode<128, true>(a, mode, st);
   if (d == 64) return launch_mode<64, false>(a, mode, st);
   return launch_mode<128, false>(a, mode, st);

@@ -52,6 +52,9 @@ struct AttnArgs {
   const int32_t* win_idx;
   const int32_t* tile_order;
   int n_tiles, tile_tokens;
+  // dense over listed key tiles (mode 3): ascending BN-key tile indices
+  const int32_t* key_tiles;
+  int n_key_tiles;
 };
 
 constexpr int kBM = 128;      // queries per workgroup (4 waves x 32)
@@ -59,7 +62,7 @@ constexpr int kBN = 64;       // keys per online-softmax step
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
 hipError_t launch_count_nonfinite(const float* x, int64_t n, int32_t* count, hipStream_t st);
-// mode: 0 dense, 1 causal, 2 sliding-tile
+// mode: 0 dense, 1 causal, 2 sliding-tile, 3 dense over listed key tiles
 // v4: V in MXFP4 along tokens (FP4 P.V; MXFP4 Q/K, d = 128)
 hipError_t launch_attention(const AttnArgs& a, int d, bool mx, bool v4, int mode, hipStream_t st);
 

@@ -45,7 +45,9 @@ def kernel_positions(plan, tokens):
 
 def head_job(job):
     """(config name, shm names, shape, head, raster tokens, bn) ->
-    (head, tokens, oracle rows [len, d] float32, digests)."""
+    (head, tokens, oracle rows [len, d] float32, digests, unquantised rows).
+    The unquantised rows are exact softmax attention of the bf16 inputs
+    themselves (float64), the path the quantised recipe approximates."""
     name, shm_names, shape, head, tokens, bn = job
     cfg = CONFIGS[name]
     blocks = [shared_memory.SharedMemory(name=n) for n in shm_names]
@@ -88,7 +90,24 @@ def head_job(job):
     else:
         out[:] = OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm, bn=bn,
                                      causal=cfg.mode == "causal", kv_valid=kv_valid)
-    return head, tokens, out, digests
+    return head, tokens, out, digests, unquantised_rows(cfg, plan, q, k, v, rows, sm)
+
+
+def unquantised_rows(cfg, plan, q, k, v, rows, sm):
+    """softmax(q k^T sm) v for the given kernel-order rows in float64, with the
+    workload's key set (causal prefix, sliding-tile window, padding mask)."""
+    n = q.shape[0]
+    keep = np.ones((len(rows), n), bool)
+    if cfg.mode == "causal":
+        keep &= np.arange(n)[None, :] <= rows[:, None]
+    if plan is not None:
+        keep &= plan.kv_valid.astype(bool)[None, :]
+        if cfg.mode == "sta":
+            tiles = np.arange(n) // plan.tile_tokens
+            for x, r in enumerate(rows):
+                u = r // plan.tile_tokens
+                keep[x] &= np.isin(tiles, plan.win_idx[plan.win_off[u]:plan.win_off[u + 1]])
+    return OA.brute_force(q[rows], k, v, sm, mask=keep).astype(np.float32)
 
 
 U_BF16 = 2.0 ** -8

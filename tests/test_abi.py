@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(B):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(B.lib(), name), name
-    assert B.lib().pab_abi_version() == 3
+    assert B.lib().pab_abi_version() == 4
 
 
 def test_token_alloc_and_info(B):
@@ -157,6 +157,40 @@ def test_backward_validation_without_device(B):
     assert bwd(q=mk(0, d=64), k=mk(0, d=64), v=mk(1, d=64)) == B.PAB_UNSUPPORTED
     assert bwd(k=mk(2)) == B.PAB_INVALID_ARG                          # mixed Q/K recipes
     assert bwd(q=mk(0, op=0)) == B.PAB_INVALID_ARG                    # FP8 Q without operand copy
+    assert L.pab_last_hip_error() == 0
+
+
+def test_key_tiles_helper(B):
+    """pab_key_tiles lists the BN-key tiles holding a nonzero byte."""
+    rng = np.random.default_rng(3)
+    bn = B.attention_info("fp8_block", 128, 0)[1]
+    for n in (1, 64, 65, 1000, 4096 + 17):
+        kv = (rng.random(n) < 0.3).astype(np.uint8)
+        kv[: min(n, 2 * bn)] = 0                 # two empty tiles at the front
+        want = [t for t in range(-(-n // bn)) if kv[t * bn:(t + 1) * bn].any()]
+        assert list(B.key_tiles(kv)) == want
+    L = B.lib()
+    cnt = ctypes.c_int64()
+    kv = np.ones(10, np.uint8)
+    assert L.pab_key_tiles(kv.ctypes.data, 10, bn + 1, None, ctypes.byref(cnt)) == B.PAB_INVALID_ARG
+    assert L.pab_key_tiles(None, 10, bn, None, ctypes.byref(cnt)) == B.PAB_INVALID_ARG
+
+
+def test_dense_tiles_validation_without_device(B):
+    L = B.lib()
+    fake = 4096
+    mk = lambda recipe, n=256, d=128, blk=128, op=fake: B.QView(fake, fake, op, recipe, blk, 1, 2, n, d)
+    qv, kv, vv = mk(0), mk(0), mk(1)
+    st = B._i64([2 * 256 * 128, 256 * 128, 128, 1])
+    null = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(fake)
+    call = lambda tiles=f, n_tiles=2, kvv=f: L.pab_attention_dense_tiles(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, 0, tiles, n_tiles, kvv, null, 256,
+        f, st, null, null)
+    assert call(tiles=null) == B.PAB_INVALID_ARG
+    assert call(kvv=null) == B.PAB_INVALID_ARG                 # skipped keys must be masked
+    assert call(n_tiles=0) == B.PAB_INVALID_ARG
+    assert call(n_tiles=5) == B.PAB_INVALID_ARG                # more tiles than N holds
     assert L.pab_last_hip_error() == 0
 
 

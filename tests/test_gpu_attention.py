@@ -269,3 +269,44 @@ def test_fp4_pv_sta(gpu_lib):
             ref[0, h, op.perm[rows][keep]] = o[keep]
     mx, mean = assert_close(got, ref, "fp4 p.v sta")
     print("  max-abs %.3g mean-abs %.3g" % (mx, mean))
+
+
+@pytest.mark.parametrize("case", [
+    dict(recipe="fp8", d=128, blk=128),   # ping-pong kernel
+    dict(recipe="mxfp4", d=128, blk=32),  # 4-wave kernel
+    dict(recipe="fp8", d=64, blk=64),
+])
+def test_dense_key_tiles_equal_dense(gpu_lib, case):
+    """Visiting only the key tiles that hold a valid key gives the dense result
+    bit for bit (a tile without a valid key leaves the online softmax as it
+    is); a query block stored nowhere is skipped without touching the rest."""
+    B, H, N, d = 1, 2, 1000, case["d"]
+    x, ts = _inputs(B, H, N, d, 70)
+    dev = [t.cuda() for t in ts]
+    if case["recipe"] == "fp8":
+        q = gpu_lib.quantize(dev[0], "fp8_block", case["blk"])
+        k = gpu_lib.quantize(dev[1], "fp8_block", case["blk"])
+    else:
+        q = gpu_lib.quantize(dev[0], "mxfp4")
+        k = gpu_lib.quantize(dev[1], "mxfp4")
+    v = gpu_lib.quantize(dev[2], "fp8_channel")
+    bn = gpu_lib.attention_info("fp8_block" if case["recipe"] == "fp8" else "mxfp4", d, 0)[1]
+    kv = np.ones(N, np.uint8)
+    for t in (0, 2, 5, 6, 15):                     # whole tiles of padding (15: the ragged tail)
+        kv[t * bn:(t + 1) * bn] = 0
+    kv[np.random.default_rng(71).permutation(N)[:50]] = 0
+    perm = np.arange(N, dtype=np.int32)
+    perm[256:384] = -1                             # a query block stored nowhere
+    tiles = gpu_lib.key_tiles(kv)
+    assert 0 not in tiles and 15 not in tiles and len(tiles) == -(-N // bn) - 5
+    kvd, permd, tilesd = (torch.from_numpy(a).cuda() for a in (kv, perm, tiles))
+    ref = torch.zeros((B, H, N, d), dtype=torch.float32, device="cuda")
+    got = torch.zeros_like(ref)
+    gpu_lib.attention_dense(q, k, v, kv_valid=kvd, out_perm=permd, out=ref)
+    gpu_lib.attention_dense(q, k, v, kv_valid=kvd, out_perm=permd, out=got, key_tiles=tilesd)
+    ref_l, ref_lse = gpu_lib.attention_dense(q, k, v, kv_valid=kvd, lse=True)
+    got_l, got_lse = gpu_lib.attention_dense(q, k, v, kv_valid=kvd, lse=True, key_tiles=tilesd)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert torch.all(got[:, :, 256:384] == 0)
+    assert torch.equal(got_l, ref_l) and torch.equal(got_lse, ref_lse)

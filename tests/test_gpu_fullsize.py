@@ -46,7 +46,7 @@ def _gpu_run(lib, cfg, x):
         out = lib.attention_sta(qq, kq, vq, dplan)
     elif dplan is not None:
         out = lib.attention_dense(qq, kq, vq, kv_valid=dplan.kv_valid, out_perm=dplan.perm,
-                                  n_out=cfg.n_real)
+                                  n_out=cfg.n_real, key_tiles=dplan.key_tiles)
     else:
         out = lib.attention_dense(qq, kq, vq, causal=cfg.mode == "causal")
     torch.cuda.synchronize()
@@ -108,7 +108,8 @@ def test_full_size_sampled_rows(gpu_lib, name):
             s.unlink()
     print("  oracle done", flush=True)
     worst, total, count = 0.0, 0.0, 0
-    for head, toks, ref, dig in results:
+    uq_worst, uq_total = 0.0, 0.0
+    for head, toks, ref, dig, unq in results:
         assert _gpu_digests(cfg, qq, kq, vq, head) == dig, "codes or scales differ, head %d" % head
         got = out[0, head, torch.from_numpy(toks).to(out.device)].cpu().numpy()
         assert np.all(np.isfinite(got)), "non-finite output, head %d" % head
@@ -116,6 +117,13 @@ def test_full_size_sampled_rows(gpu_lib, name):
         worst = max(worst, float(err.max()))
         total += float(err.sum())
         count += err.size
+        uerr = np.abs(got.astype(np.float64) - unq.astype(np.float64))
+        uq_worst = max(uq_worst, float(uerr.max()))
+        uq_total += float(uerr.sum())
     mean = total / count
     print("  %s: %d rows, max-abs %.3g mean-abs %.3g" % (name, len(heads), worst, mean), flush=True)
+    # reported, not gated (the pages give no figure for the recipe's own error):
+    # the library's output against exact attention of the unquantised bf16 inputs
+    print("  %s against the unquantised bf16-input attention: max-abs %.3g mean-abs %.3g" % (
+        name, uq_worst, uq_total / count), flush=True)
     assert worst <= MAX_ABS and mean <= MEAN_ABS, (worst, mean)
