@@ -148,7 +148,7 @@ class GpuPath:
     def attend(self, qq, kq, vq):
         cfg, lib = self.cfg, self.lib
         if cfg.mode == "sta":
-            return lib.attention_sta(qq, kq, vq, self.dplan, out=self.out, tau=self.tau)
+            return lib.attention_sta(qq, kq, vq, self.dplan, out=self.out, tau=self.tau, steps=True)
         if self.dplan is not None:
             return lib.attention_dense(qq, kq, vq, kv_valid=self.dplan.kv_valid,
                                        out_perm=self.dplan.perm, n_out=cfg.n_real, out=self.out,

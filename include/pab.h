@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define PAB_ABI_VERSION 4
+#define PAB_ABI_VERSION 5
 #define PAB_TOKEN_ALIGN 128  /* query tile of the attention kernel */
 #define PAB_MAX_TAU 8        /* largest softmax rescale threshold (log2 units) */
 
@@ -240,6 +240,32 @@ pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_q
                              const uint8_t* kv_valid, const int32_t* out_perm,
                              int64_t n_out_tokens, float* out, const int64_t out_strides[4],
                              float* lse, void* stream);
+
+/*
+ * pab_attention_sta_steps - pab_attention_sta with window lists in BN-key
+ * steps instead of whole key tiles: query tile u visits the BN-key tiles
+ * step_idx[step_off[u] .. step_off[u+1]-1] (ascending; tile t = keys t*BN ..
+ * t*BN+BN-1).  pab_sta_steps expands tile window lists into these and drops
+ * the steps without a valid key, which leaves the result unchanged (bit for
+ * bit): a padded grid then skips its padding keys.
+ */
+pab_status pab_attention_sta_steps(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                   float sm_scale, int tau, const int32_t* step_off,
+                                   const int32_t* step_idx, const int32_t* tile_order, int n_tiles,
+                                   int tile_tokens, const uint8_t* kv_valid,
+                                   const int32_t* out_perm, int64_t n_out_tokens, float* out,
+                                   const int64_t out_strides[4], float* lse, void* stream);
+
+/*
+ * pab_sta_steps - host helper: expands the window lists of pab_sta_plan
+ * (win_off [n_tiles+1], win_idx) into BN-key step lists, keeping the steps
+ * that hold a valid key of kv_valid (host uint8 [n], NULL = all valid), in
+ * ascending order.  n = n_tiles * tile_tokens.  Two-call pattern: with
+ * step_off / step_idx NULL only *n_steps is returned.
+ */
+pab_status pab_sta_steps(const int32_t* win_off, const int32_t* win_idx, int n_tiles,
+                         int tile_tokens, const uint8_t* kv_valid, int64_t n, int bn,
+                         int32_t* step_off, int32_t* step_idx, int64_t* n_steps);
 
 /*
  * pab_attention_backward - gradients of the attention of pab_attention_dense

@@ -23,6 +23,7 @@ EXPORTS = [
     "pab_attention_info", "pab_quantize", "pab_attention_dense", "pab_attention_sta",
     "pab_sta_plan", "pab_count_nonfinite", "pab_attention_backward_workspace",
     "pab_attention_backward", "pab_attention_dense_tiles", "pab_key_tiles",
+    "pab_attention_sta_steps", "pab_sta_steps",
 ]
 
 
@@ -77,6 +78,11 @@ def _lib():
         L.pab_attention_dense_tiles.restype = ctypes.c_int
         L.pab_attention_dense_tiles.argtypes = [ctypes.POINTER(QView)] * 3 + [
             ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp, vp, ctypes.c_int64, vp, i64p, vp, vp]
+        L.pab_attention_sta_steps.restype = ctypes.c_int
+        L.pab_attention_sta_steps.argtypes = list(L.pab_attention_sta.argtypes)
+        L.pab_sta_steps.restype = ctypes.c_int
+        L.pab_sta_steps.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int64, ctypes.c_int,
+                                    vp, vp, i64p]
         L.pab_key_tiles.restype = ctypes.c_int
         L.pab_key_tiles.argtypes = [vp, ctypes.c_int64, ctypes.c_int, vp, i64p]
         L.pab_attention_backward_workspace.restype = ctypes.c_int64
@@ -250,24 +256,28 @@ def attention_dense(q, k, v, causal=False, sm_scale=None, kv_valid=None, out_per
 
 
 def attention_sta(q, k, v, plan, sm_scale=None, use_kv_valid=True, use_out_perm=True, n_out=None,
-                  out=None, tau=0, lse=None):
+                  out=None, tau=0, lse=None, steps=False):
     """Sliding-tile attention with a DevicePlan (see sta_plan / DevicePlan);
-    lse as in attention_dense."""
+    lse as in attention_dense.  steps: walk the plan's BN-key step lists,
+    which leave out the steps without a valid key (pab_attention_sta_steps;
+    same result, less work on a padded grid)."""
     n_out = plan.n_real if n_out is None else int(n_out)
     if not use_out_perm and n_out is None:
         n_out = q.N
     out = _out_tensor(q, n_out, out)
     lse_t = _lse_tensor(q, lse)
     qv, kv, vv = q.view(), k.view(), v.view()
-    st = _lib().pab_attention_sta(
+    fn = _lib().pab_attention_sta_steps if steps else _lib().pab_attention_sta
+    off, idx = (plan.step_off, plan.step_idx) if steps else (plan.win_off, plan.win_idx)
+    st = fn(
         ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(sm_scale or 0.0), int(tau),
-        ctypes.c_void_p(plan.win_off.data_ptr()), ctypes.c_void_p(plan.win_idx.data_ptr()),
+        ctypes.c_void_p(off.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
         ctypes.c_void_p(plan.lpt.data_ptr()), int(plan.n_tiles), int(plan.tile_tokens),
         ctypes.c_void_p(plan.kv_valid.data_ptr() if use_kv_valid else 0),
         ctypes.c_void_p(plan.perm.data_ptr() if use_out_perm else 0), n_out,
         ctypes.c_void_p(out.data_ptr()), _i64(out.stride()),
         ctypes.c_void_p(lse_t.data_ptr() if lse_t is not None else 0), _stream(out.device))
-    _check(st, "pab_attention_sta")
+    _check(st, "pab_attention_sta_steps" if steps else "pab_attention_sta")
     return (out, lse_t) if lse_t is not None else out
 
 
@@ -303,6 +313,24 @@ def attention_backward(q, k, v, out, dout, lse, causal=False, sm_scale=None, kv_
         ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(dev))
     _check(st, "pab_attention_backward")
     return dq, dk, dv
+
+
+def sta_steps(hp):
+    """BN-key step lists (step_off, step_idx) of a HostPlan's windows, without
+    the steps that hold no valid key (pab_sta_steps)."""
+    bn = attention_info("fp8_block", 128, 0)[1]
+    wo = np.ascontiguousarray(hp.win_off, np.int32)
+    wi = np.ascontiguousarray(hp.win_idx, np.int32)
+    kv = np.ascontiguousarray(hp.kv_valid, np.uint8)
+    cnt = ctypes.c_int64()
+    args = (wo.ctypes.data, wi.ctypes.data, int(hp.n_tiles), int(hp.tile_tokens), kv.ctypes.data,
+            kv.size, bn)
+    _check(_lib().pab_sta_steps(*args, None, None, ctypes.byref(cnt)), "pab_sta_steps")
+    off = np.zeros(int(hp.n_tiles) + 1, np.int32)
+    idx = np.zeros(max(cnt.value, 1), np.int32)
+    _check(_lib().pab_sta_steps(*args, off.ctypes.data, idx.ctypes.data, ctypes.byref(cnt)),
+           "pab_sta_steps")
+    return off, idx
 
 
 class HostPlan:
@@ -343,8 +371,11 @@ class DevicePlan:
         import torch
         for name in ("perm", "inv_perm", "kv_valid", "win_off", "win_idx", "lpt"):
             setattr(self, name, torch.from_numpy(getattr(hp, name)).to(device))
-        # key tiles holding a valid key, for dense attention on the padded grid
+        # key tiles holding a valid key, for dense attention on the padded grid,
+        # and the window lists in BN-key steps without the padding steps
         self.key_tiles = torch.from_numpy(key_tiles(hp.kv_valid)).to(device)
+        so, si = sta_steps(hp)
+        self.step_off, self.step_idx = (torch.from_numpy(a).to(device) for a in (so, si))
         self.n_tokens, self.n_tiles, self.n_pairs = hp.n_tokens, hp.n_tiles, hp.n_pairs
         self.tile_tokens, self.n_real = hp.tile_tokens, hp.n_real
 

@@ -273,12 +273,15 @@ pab_status pab_key_tiles(const uint8_t* kv_valid, int64_t n, int bn, int32_t* ti
   return PAB_OK;
 }
 
-pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_qview* v,
-                             float sm_scale, int tau, const int32_t* win_off, const int32_t* win_idx,
-                             const int32_t* tile_order, int n_tiles, int tile_tokens,
-                             const uint8_t* kv_valid, const int32_t* out_perm,
-                             int64_t n_out_tokens, float* out, const int64_t out_strides[4],
-                             float* lse, void* stream) {
+namespace {
+
+// Sliding-tile attention with window-list entries of key_unit keys (a whole
+// key tile, or one BN-key step).
+pab_status run_sta(const pab_qview* q, const pab_qview* k, const pab_qview* v, float sm_scale, int tau,
+                   const int32_t* win_off, const int32_t* win_idx, const int32_t* tile_order,
+                   int n_tiles, int tile_tokens, int key_unit, const uint8_t* kv_valid,
+                   const int32_t* out_perm, int64_t n_out_tokens, float* out,
+                   const int64_t out_strides[4], float* lse, void* stream) {
   if (!win_off || !win_idx || !tile_order) return PAB_INVALID_ARG;
   if (lse && !aligned(lse, 4)) return PAB_INVALID_ARG;
   if (n_tiles < 1 || tile_tokens < PAB_TOKEN_ALIGN || tile_tokens % PAB_TOKEN_ALIGN)
@@ -294,10 +297,66 @@ pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_q
   a.tile_order = tile_order;
   a.n_tiles = n_tiles;
   a.tile_tokens = tile_tokens;
+  a.key_unit = key_unit;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(pab::launch_attention(a, (int)q->d, q->recipe == PAB_MXFP4_D32,
                                           v->recipe == PAB_MXFP4_V, 2, st),
                     st);
+}
+
+}  // namespace
+
+pab_status pab_attention_sta(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                             float sm_scale, int tau, const int32_t* win_off, const int32_t* win_idx,
+                             const int32_t* tile_order, int n_tiles, int tile_tokens,
+                             const uint8_t* kv_valid, const int32_t* out_perm,
+                             int64_t n_out_tokens, float* out, const int64_t out_strides[4],
+                             float* lse, void* stream) {
+  return run_sta(q, k, v, sm_scale, tau, win_off, win_idx, tile_order, n_tiles, tile_tokens,
+                 tile_tokens, kv_valid, out_perm, n_out_tokens, out, out_strides, lse, stream);
+}
+
+pab_status pab_attention_sta_steps(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                   float sm_scale, int tau, const int32_t* step_off,
+                                   const int32_t* step_idx, const int32_t* tile_order, int n_tiles,
+                                   int tile_tokens, const uint8_t* kv_valid,
+                                   const int32_t* out_perm, int64_t n_out_tokens, float* out,
+                                   const int64_t out_strides[4], float* lse, void* stream) {
+  return run_sta(q, k, v, sm_scale, tau, step_off, step_idx, tile_order, n_tiles, tile_tokens,
+                 pab::kBN, kv_valid, out_perm, n_out_tokens, out, out_strides, lse, stream);
+}
+
+pab_status pab_sta_steps(const int32_t* win_off, const int32_t* win_idx, int n_tiles,
+                         int tile_tokens, const uint8_t* kv_valid, int64_t n, int bn,
+                         int32_t* step_off, int32_t* step_idx, int64_t* n_steps) {
+  if (!win_off || !win_idx || !n_steps || n_tiles < 1 || bn != pab::kBN || tile_tokens < bn ||
+      tile_tokens % bn || (int64_t)n_tiles * tile_tokens != n)
+    return PAB_INVALID_ARG;
+  const int spt = tile_tokens / bn;
+  auto valid = [&](int64_t kt) {
+    if (!kv_valid) return true;
+    for (int64_t j = kt * bn; j < (kt + 1) * bn; ++j)
+      if (kv_valid[j]) return true;
+    return false;
+  };
+  int64_t c = 0;
+  for (int u = 0; u < n_tiles; ++u) {
+    if (step_off) step_off[u] = (int32_t)c;
+    if (win_off[u] > win_off[u + 1]) return PAB_INVALID_ARG;
+    for (int32_t e = win_off[u]; e < win_off[u + 1]; ++e) {
+      const int32_t w = win_idx[e];
+      if (w < 0 || w >= n_tiles) return PAB_INVALID_ARG;
+      for (int s = 0; s < spt; ++s) {
+        const int64_t kt = (int64_t)w * spt + s;
+        if (!valid(kt)) continue;
+        if (step_idx) step_idx[c] = (int32_t)kt;
+        ++c;
+      }
+    }
+  }
+  if (step_off) step_off[n_tiles] = (int32_t)c;
+  *n_steps = c;
+  return PAB_OK;
 }
 
 int64_t pab_attention_backward_workspace(int64_t B, int64_t H, int64_t N, int64_t d) {

@@ -220,7 +220,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int work = xcd_work_index(blockIdx.x, gridDim.x);
 
   int bh, q0, n_steps, u = 0;
-  const int spt = MODE == 2 ? a.tile_tokens / kBN : 1;
+  // steps per window-list entry: an entry is a whole key tile (key_unit =
+  // tile_tokens) or one BN-key step (key_unit = BN)
+  const int spt = MODE == 2 ? a.key_unit / kBN : 1;
   if (MODE == 2) {
     const int sub = a.tile_tokens / kBM;               // query tiles per window tile
     const int per_bh = a.n_tiles * sub;
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const_i32* wlist = MODE == 2 ? (const_i32*)(a.win_idx + a.win_off[u])
                      : MODE == 3 ? (const_i32*)a.key_tiles : nullptr;
   auto step_start = [&](int t) -> int {
-    if (MODE == 2) return wlist[t / spt] * a.tile_tokens + (t % spt) * kBN;
+    if (MODE == 2) return wlist[t / spt] * a.key_unit + (t % spt) * kBN;
     if (MODE == 3) return wlist[t] * kBN;
     return t * kBN;
   };

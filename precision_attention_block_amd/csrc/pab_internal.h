@@ -52,6 +52,7 @@ struct AttnArgs {
   const int32_t* win_idx;
   const int32_t* tile_order;
   int n_tiles, tile_tokens;
+  int key_unit;               // keys per window-list entry: tile_tokens, or BN (step lists)
   // dense over listed key tiles (mode 3): ascending BN-key tile indices
   const int32_t* key_tiles;
   int n_key_tiles;

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(B):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(B.lib(), name), name
-    assert B.lib().pab_abi_version() == 4
+    assert B.lib().pab_abi_version() == 5
 
 
 def test_token_alloc_and_info(B):
@@ -192,6 +192,26 @@ def test_dense_tiles_validation_without_device(B):
     assert call(n_tiles=0) == B.PAB_INVALID_ARG
     assert call(n_tiles=5) == B.PAB_INVALID_ARG                # more tiles than N holds
     assert L.pab_last_hip_error() == 0
+
+
+def test_sta_steps_helper(B):
+    """pab_sta_steps expands each window into its BN-key steps, ascending, and
+    drops the steps without a valid key."""
+    bn = B.attention_info("fp8_block", 128, 0)[1]
+    hp = B.sta_plan((8, 16, 16), (7, 13, 16), (4, 8, 8), (3, 3, 3))
+    off, idx = B.sta_steps(hp)
+    spt = hp.tile_tokens // bn
+    for u in range(hp.n_tiles):
+        want = [w * spt + s for w in hp.win_idx[hp.win_off[u]:hp.win_off[u + 1]] for s in range(spt)
+                if hp.kv_valid[(w * spt + s) * bn:(w * spt + s + 1) * bn].any()]
+        assert list(idx[off[u]:off[u + 1]]) == want
+    assert off[-1] < len(hp.win_idx) * spt        # the padded grid loses some steps
+    L = B.lib()
+    cnt = ctypes.c_int64()
+    wo, wi = hp.win_off.copy(), hp.win_idx.copy()
+    wi[0] = hp.n_tiles                               # window tile out of range
+    assert L.pab_sta_steps(wo.ctypes.data, wi.ctypes.data, hp.n_tiles, hp.tile_tokens, None,
+                           hp.n_tokens, bn, None, None, ctypes.byref(cnt)) == B.PAB_INVALID_ARG
 
 
 def test_planner_validation(B):

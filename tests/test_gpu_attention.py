@@ -129,7 +129,7 @@ def _sta_setup(lib, grid, real, tile, window, H=2, seed=40, outl=True):
     return hp, op, x, ts
 
 
-def _run_sta(lib, hp, ts, window_plan=None, dense=False, tau=0):
+def _run_sta(lib, hp, ts, window_plan=None, dense=False, tau=0, steps=False):
     dp = lib.DevicePlan(hp if window_plan is None else window_plan)
     dev = [t.cuda() for t in ts]
     q = lib.quantize(dev[0], "fp8_block", hp.tile_tokens, perm=dp.perm, n_out=dp.n_tokens)
@@ -139,7 +139,7 @@ def _run_sta(lib, hp, ts, window_plan=None, dense=False, tau=0):
         out = lib.attention_dense(q, k, v, kv_valid=dp.kv_valid, out_perm=dp.perm, n_out=dp.n_real,
                                   tau=tau)
     else:
-        out = lib.attention_sta(q, k, v, dp, tau=tau)
+        out = lib.attention_sta(q, k, v, dp, tau=tau, steps=steps)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -164,6 +164,9 @@ def test_sta_parity_with_padding(gpu_lib, window, tau):
             keep = op.perm[rows] >= 0
             ref[0, h, op.perm[rows][keep]] = o[keep]
     assert_close(got, ref, "sta %s" % (window,))
+    # window lists in BN-key steps without the padding steps: the same bits
+    # (the last frame of every tile in the last tile row is padding here)
+    assert np.array_equal(_run_sta(gpu_lib, hp, ts, tau=tau, steps=True), got)
 
 
 @pytest.mark.parametrize("grid,real,tile,window", [

@@ -43,7 +43,7 @@ def _gpu_run(lib, cfg, x):
     vq = lib.quantize(v, "mxfp4_v" if cfg.recipe == "mxfp4_pv" else "fp8_channel", None, perm, n_out)
     del q, k, v
     if cfg.mode == "sta":
-        out = lib.attention_sta(qq, kq, vq, dplan)
+        out = lib.attention_sta(qq, kq, vq, dplan, steps=True)
     elif dplan is not None:
         out = lib.attention_dense(qq, kq, vq, kv_valid=dplan.kv_valid, out_perm=dplan.perm,
                                   n_out=cfg.n_real, key_tiles=dplan.key_tiles)
