@@ -201,7 +201,7 @@ __device__ inline float max3f(float a, float b, float c) { return fmaxf(fmaxf(a,
 // V4: FP4 P.V - V in MXFP4 along tokens and P requantised to MXFP4 per 32
 // keys (MXFP4 Q/K only).
 template <int D, bool MX, int MODE, bool UK, bool V4>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using TL = Tile<D, MX, V4>;
   constexpr int DB = D / 32;            // 32-channel blocks of O^T
@@ -279,7 +279,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     if (MX) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+        // E2M1 operands occupy the lower four registers; the upper four are
+        // never read and stay unset
+        v8i r;
         const uint4 x = *reinterpret_cast<const uint4*>(a.q + qrow * (D / 2) + 16 * (2 * i + lg));
         r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
         qop8[i] = r;
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       if (MX) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          v8i kr = {0, 0, 0, 0, 0, 0, 0, 0};
+          v8i kr;   // E2M1: only the lower four registers are read
           const uint4 x = *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]);
           kr[0] = x.x; kr[1] = x.y; kr[2] = x.z; kr[3] = x.w;
           const int ksc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       if (MX) op.sc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
     }
   };
-  auto issue_op = [&](const int m, const Op& op, v16f (&acc)[2], const v8i& pk_in,
+  auto issue_op = [&](const int m, const Op& op, v16f& acc0, v16f& acc1, const v8i& pk_in,
                       const uint32_t vsc, const int ps_in) __attribute__((always_inline)) {
     if (m < DB) {
       pv_mfma(m, op.a, pk_in, vsc, ps_in);
@@ -441,15 +443,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) c0[j] = 0.0f;
       if (MX) {
-        v8i kr = {0, 0, 0, 0, 0, 0, 0, 0};
+        v8i kr;   // E2M1: only the lower four registers are read
         kr[0] = op.a[0]; kr[1] = op.a[1]; kr[2] = op.a[2]; kr[3] = op.a[3];
-        acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], i == 0 ? c0 : acc[kb],
+        v16f& acc = kb == 0 ? acc0 : acc1;
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], i == 0 ? c0 : acc,
                                                                   4, 4, 0, op.sc, 0, qsc[i]);
       } else {
         v8s kr;
         const v4i x = {op.a[0], op.a[1], op.a[2], op.a[3]};
         kr = __builtin_bit_cast(v8s, x);
-        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qop16[i], i == 0 ? c0 : acc[kb], 0, 0, 0);
+        v16f& acc = kb == 0 ? acc0 : acc1;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qop16[i], i == 0 ? c0 : acc, 0, 0, 0);
       }
     }
   };
@@ -473,8 +477,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   wait_vm_le<NV + NK>();          // V(0) and K(2) may still be in flight
   barrier_lds();
 
-  v16f sa[2], sb[2];
-  qk(k0, sa);
+  // Score tiles: S(t) = (c0, c1) and S(t+1) = (n0, n1).  MXFP4 forms the
+  // next tile's key block 0 in slots 4-5, after this tile's block 0 has been
+  // read (slots 0-3), so the two share registers (ga): three tiles rotate
+  // instead of four, which saves 16 registers.  FP8 starts block 0 in slot 1.
+  v16f ga[2], gb[2], gc;
+  qk(k0, ga);
   // P~ of the previous tile (read by the P.V MFMAs) and of the current one
   // alternate between pa and pb like the score buffers
   v8i pa = {0, 0, 0, 0, 0, 0, 0, 0}, pb = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -485,9 +493,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // Iteration t: K stages Kr (t+1, read) and Kw (t+3, written); V stages Vr
   // (t-1, read) and Vw (t+1, written); side stages Ar (t, read), Aw (t+2, written).
   auto iter = [&](const int t, const uint8_t* Kr, uint8_t* Kw, const uint8_t* Vr, uint8_t* Vw,
-                  const uint8_t* Ar, uint8_t* Aw, v16f (&s_cur)[2], v16f (&s_nxt)[2],
+                  const uint8_t* Ar, uint8_t* Aw, v16f& c0s, v16f& c1s, v16f& n0s, v16f& n1s,
                   const v8i& pk_in, v8i& pk, const int ps_in, int& ps_out)
       __attribute__((always_inline)) {
+    auto s_cur = [&](int kb) __attribute__((always_inline)) -> v16f& { return kb == 0 ? c0s : c1s; };
     const int ks = step_start(t);
     // this iteration's copies (K(t+3), V(t+1), side data of t+2) are issued
     // one instruction per slot below: issued back to back by every wave they
@@ -557,7 +566,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
             for (int jj = 0; jj < 4; ++jj) {
               const int key = ks + 32 * kb + 8 * g4 + 4 * lg + jj;
               const bool ok = (key <= lim) & (((w >> (8 * jj)) & 0xFFu) != 0u);
-              s_cur[kb][4 * g4 + jj] = ok ? s_cur[kb][4 * g4 + jj] : kNegInf;
+              s_cur(kb)[4 * g4 + jj] = ok ? s_cur(kb)[4 * g4 + jj] : kNegInf;
             }
           }
       }
@@ -576,7 +585,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     if (V4) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const v16f& x = s_cur[kb];
+        const v16f& x = s_cur(kb);
         const float t0 = max3f(x[0], x[1], x[2]), t1 = max3f(x[3], x[4], x[5]);
         const float t2 = max3f(x[6], x[7], x[8]), t3 = max3f(x[9], x[10], x[11]);
         const float t4 = max3f(x[12], x[13], x[14]);
@@ -589,10 +598,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 10; ++i) {
         const int e = 3 * i;
-        m11[i] = max3f(s_cur[e / 16][e % 16], s_cur[(e + 1) / 16][(e + 1) % 16],
-                       s_cur[(e + 2) / 16][(e + 2) % 16]);
+        m11[i] = max3f(s_cur(e / 16)[e % 16], s_cur((e + 1) / 16)[(e + 1) % 16],
+                       s_cur((e + 2) / 16)[(e + 2) % 16]);
       }
-      m11[10] = fmaxf(s_cur[1][14], s_cur[1][15]);
+      m11[10] = fmaxf(s_cur(1)[14], s_cur(1)[15]);
       const float m = max3f(max3f(m11[0], m11[1], m11[2]), max3f(m11[3], m11[4], m11[5]),
                             max3f(max3f(m11[6], m11[7], m11[8]), m11[9], m11[10]));
       mx = c[0] * m;
@@ -602,8 +611,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const float m4 = fmaxf(fmaxf(s_cur[kb][4 * g4], s_cur[kb][4 * g4 + 1]),
-                                 fmaxf(s_cur[kb][4 * g4 + 2], s_cur[kb][4 * g4 + 3]));
+          const float m4 = fmaxf(fmaxf(s_cur(kb)[4 * g4], s_cur(kb)[4 * g4 + 1]),
+                                 fmaxf(s_cur(kb)[4 * g4 + 2], s_cur(kb)[4 * g4 + 3]));
           mx = fmaxf(mx, c[4 * kb + g4] * m4);
         }
     }
@@ -644,7 +653,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // with empty volatile asm statements (kept in program order): a slot's
     // MFMAs take their operands from one, and its exponentials end in one.
     float gs[8];
-    v16f acc[2];
     float pq[4];   // exponentials of the previous group, packed one slot later
     uint32_t pk4[4];   // FP4 P.V: E2M1 codes, 8 per dword, dwords 0-1 key group 0
     // packs group g's four P values (E4M3, or E2M1 for FP4 P.V) and sums them;
@@ -678,8 +686,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       copy_item(g);
 #pragma unroll
       for (int m = slot_lo(g); m < slot_lo(g + 1); ++m) {
-        asm volatile("" : "+v"(ops[m].a));
-        issue_op(m, ops[m], acc, pk_in, vsc, ps_in);
+        if (MX && !V4 && m >= DB) {
+          // an E2M1 K operand lives in its lower four registers
+          v4i lo = {ops[m].a[0], ops[m].a[1], ops[m].a[2], ops[m].a[3]};
+          asm volatile("" : "+v"(lo));
+          ops[m].a[0] = lo[0]; ops[m].a[1] = lo[1]; ops[m].a[2] = lo[2]; ops[m].a[3] = lo[3];
+        } else {
+          asm volatile("" : "+v"(ops[m].a));
+        }
+        issue_op(m, ops[m], n0s, n1s, pk_in, vsc, ps_in);
       }
 #pragma unroll
       for (int m = slot_lo(g + LA); m < slot_lo(g + LA + 1); ++m) read_op(m, Vr, Kr, ops[m]);
@@ -689,14 +704,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       float pn[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        pn[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[kb][4 * g4 + j], cc, -sh));
+        pn[j] = __builtin_amdgcn_exp2f(fmaf(s_cur(kb)[4 * g4 + j], cc, -sh));
       if (g > 0) finish(g - 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) pq[j] = pn[j];
     }
     finish(7);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_nxt[kb] = acc[kb];
     float sum;
     if (V4) {
       // B operand of the FP4 P.V product: lane half lg takes key group lg, its
@@ -721,12 +734,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // unrolled by 6: the stage rings have period 3 and the two score buffers
   // alternate, so no buffer is ever copied
   for (int t = 0; t < n_steps; t += 6) {
-    iter(t, k1, k0, v2, v1, x0, x2, sa, sb, pa, pb, psa, psb);
-    if (t + 1 < n_steps) iter(t + 1, k2, k1, v0, v2, x1, x0, sb, sa, pb, pa, psb, psa);
-    if (t + 2 < n_steps) iter(t + 2, k0, k2, v1, v0, x2, x1, sa, sb, pa, pb, psa, psb);
-    if (t + 3 < n_steps) iter(t + 3, k1, k0, v2, v1, x0, x2, sb, sa, pb, pa, psb, psa);
-    if (t + 4 < n_steps) iter(t + 4, k2, k1, v0, v2, x1, x0, sa, sb, pa, pb, psa, psb);
-    if (t + 5 < n_steps) iter(t + 5, k0, k2, v1, v0, x2, x1, sb, sa, pb, pa, psb, psa);
+    // even t: S(t) in (ga0, ga1) -> S(t+1) in (MX ? ga0 : gb0, MX ? gc : gb1);
+    // odd t: S(t) in (MX ? ga0 : gb0, MX ? gc : gb1) -> S(t+1) in (ga0, ga1)
+    v16f& e0 = ga[0];
+    v16f& e1 = ga[1];
+    v16f& o0 = MX ? ga[0] : gb[0];
+    v16f& o1 = MX ? gc : gb[1];
+    iter(t, k1, k0, v2, v1, x0, x2, e0, e1, o0, o1, pa, pb, psa, psb);
+    if (t + 1 < n_steps) iter(t + 1, k2, k1, v0, v2, x1, x0, o0, o1, e0, e1, pb, pa, psb, psa);
+    if (t + 2 < n_steps) iter(t + 2, k0, k2, v1, v0, x2, x1, e0, e1, o0, o1, pa, pb, psa, psb);
+    if (t + 3 < n_steps) iter(t + 3, k1, k0, v2, v1, x0, x2, o0, o1, e0, e1, pb, pa, psb, psa);
+    if (t + 4 < n_steps) iter(t + 4, k2, k1, v0, v2, x1, x0, e0, e1, o0, o1, pa, pb, psa, psb);
+    if (t + 5 < n_steps) iter(t + 5, k0, k2, v1, v0, x2, x1, o0, o1, e0, e1, pb, pa, psb, psa);
   }
   // the last tile's product: V(n_steps - 1) sits in stage (n_steps - 1) % 3
   {
