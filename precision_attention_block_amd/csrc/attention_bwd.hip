@@ -495,7 +495,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---- dQ -------------------------------------------------------------------------
-template <bool CAUSAL>
+// UK: the K block scale is the same for all 32 keys of a step (MXFP4, or FP8
+// blocks of a multiple of 32 tokens).
+template <bool CAUSAL, bool UK>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __align__(16) uint8_t st0[Stage::BYTES], st1[Stage::BYTES];
@@ -551,17 +553,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int n_keys = (a.N + 31) / 32 * 32;
   const int k_end = CAUSAL ? min(qt * kBwdTile + kBwdTile, n_keys) : n_keys;
   const bool tail_mask = a.kv_valid != nullptr;
-  issue(st0, 0);
-  int it = 0;
-  for (int k0 = 0; k0 < k_end; k0 += 32, ++it) {
-    const uint8_t* cur = (it & 1) ? st1 : st0;
-    wait_vm_le<0>();
-    barrier_lds();
-    if (k0 + 32 < k_end) issue((it & 1) ? st0 : st1, k0 + 32);
-    if (CAUSAL && k0 > qw0 + 31) continue;   // every key of the step follows this wave's queries
 
-    // S^T (keys x queries) = K Q^T and dP^T = V_codes (dO / s_V)^T
-    v16f s, dp;
+  // S^T (keys x queries) = K Q^T and dP^T = V_codes (dO / s_V)^T of the step
+  // in stage `cur`; register 4 ii + r is key k0 + 8 ii + 4 lg + r
+  auto products = [&](const uint8_t* cur, v16f& s, v16f& dp) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
 #pragma unroll
@@ -571,36 +566,74 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R1, lr, 2 * ks + lg), gb[ks],
                                                    dp, 0, 0, 0);
     }
-    // register 4 ii + r is key k0 + 8 ii + 4 lg + r
-    float4 fk4[4], kv4[4];
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      fk4[ii] = *reinterpret_cast<const float4*>(cur + Stage::F0 + 4 * (8 * ii + 4 * lg));
-      kv4[ii] = *reinterpret_cast<const float4*>(cur + Stage::F1 + 4 * (8 * ii + 4 * lg));
+  };
+  // dS'^T = P^T (dP^T - D) sm / s_K and dQ^T += K_vals^T dS'^T
+  auto finish = [&](const int k0, const uint8_t* cur, const v16f& s, const v16f& dp)
+      __attribute__((always_inline)) {
+    float cs = 0.0f, sc = 0.0f;
+    if (UK) {
+      const float fk = *reinterpret_cast<const float*>(cur + Stage::F0);
+      cs = cq * fk;
+      sc = a.sm * fk;
     }
     const bool masked = tail_mask || k0 + 32 > a.N || (CAUSAL && k0 + 31 > qw0);
-    float ds[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int ii = e / 4, r = e % 4;
-      const float fk = r == 0 ? fk4[ii].x : r == 1 ? fk4[ii].y : r == 2 ? fk4[ii].z : fk4[ii].w;
-      float pe = __builtin_amdgcn_exp2f(fmaf(s[e] * cq, fk, -lse));
-      if (masked) {
-        const float kv = r == 0 ? kv4[ii].x : r == 1 ? kv4[ii].y : r == 2 ? kv4[ii].z : kv4[ii].w;
-        const int key = k0 + 8 * ii + 4 * lg + r;
-        pe = (kv != 0.0f && (!CAUSAL || key <= i)) ? pe : 0.0f;
-      }
-      ds[e] = pe * (dp[e] - ddi) * (a.sm * fk);   // dS scaled for dQ^ = sm dS K^
-    }
-    // dQ^T += K_vals^T dS'^T (channels x queries, K = keys)
+    // masked steps keep register 4 ii + r only if the key is valid and (causal)
+    // 8 ii + r <= thr, i.e. key <= query
+    const int thr = CAUSAL ? i - k0 - 4 * lg : 64;
+    v8s db[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const v8s dsb = pack_b(ds, h);
+      float ds[8];
+#pragma unroll
+      for (int x2 = 0; x2 < 2; ++x2) {
+        const int ii = 2 * h + x2;
+        float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (!UK) f4 = *reinterpret_cast<const float4*>(cur + Stage::F0 + 4 * (8 * ii + 4 * lg));
+        const float fk[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * ii + r;
+          const float pe = __builtin_amdgcn_exp2f(UK ? fmaf(s[e], cs, -lse) : fmaf(s[e] * cq, fk[r], -lse));
+          ds[4 * x2 + r] = UK ? pe * fmaf(dp[e], sc, -ddi * sc) : pe * (dp[e] - ddi) * (a.sm * fk[r]);
+        }
+      }
+      if (masked) {
+#pragma unroll
+        for (int x2 = 0; x2 < 2; ++x2) {
+          const int ii = 2 * h + x2;
+          const float4 kv4 = *reinterpret_cast<const float4*>(cur + Stage::F1 + 4 * (8 * ii + 4 * lg));
+          const float kv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool keep = kv[r] != 0.0f && 8 * ii + r <= thr;
+            ds[4 * x2 + r] = keep ? ds[4 * x2 + r] : 0.0f;
+          }
+        }
+      }
+      db[h] = __builtin_bit_cast(v8s, make_uint4(bf16x2(ds[0], ds[1]), bf16x2(ds[2], ds[3]),
+                                                 bf16x2(ds[4], ds[5]), bf16x2(ds[6], ds[7])));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
         dqt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T0, 32 * cb + lr, 2 * h + lg),
-                                                          dsb, dqt[cb], 0, 0, 0);
-    }
+                                                          db[h], dqt[cb], 0, 0, 0);
+  };
+
+  // two stages: step t+1 is copied while step t is computed.  Steps past the
+  // diagonal (causal) are computed and masked: a branch around the products
+  // makes the compiler move the accumulators on every step.
+  issue(st0, 0);
+  int it = 0;
+  for (int k0 = 0; k0 < k_end; k0 += 32, ++it) {
+    const uint8_t* cur = (it & 1) ? st1 : st0;
+    wait_vm_le<0>();
+    barrier_lds();
+    if (k0 + 32 < k_end) issue((it & 1) ? st0 : st1, k0 + 32);
+    v16f s, dp;
+    products(cur, s, dp);
+    finish(k0, cur, s, dp);
   }
   wait_vm_le<0>();
   if (i < a.N) {
@@ -634,18 +667,25 @@ hipError_t launch_attention_backward(const BwdArgs& a, hipStream_t st) {
   const dim3 gt(BH * (unsigned)(a.n_alloc / kBwdTile));
   // the Q scale is uniform over 32-query steps for MXFP4 (1) and for FP8 blocks of 32k tokens
   const bool uq = a.qk_mx || a.blk_q % 32 == 0;
+  const bool uk = a.qk_mx || a.blk_k % 32 == 0;
   if (a.causal) {
     if (uq)
       hipLaunchKernelGGL((bwd_dkdv_kernel<true, true>), gt, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<true, false>), gt, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<true>, gt, dim3(256), 0, st, a);
+    if (uk)
+      hipLaunchKernelGGL((bwd_dq_kernel<true, true>), gt, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<true, false>), gt, dim3(256), 0, st, a);
   } else {
     if (uq)
       hipLaunchKernelGGL((bwd_dkdv_kernel<false, true>), gt, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<false, false>), gt, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<false>, gt, dim3(256), 0, st, a);
+    if (uk)
+      hipLaunchKernelGGL((bwd_dq_kernel<false, true>), gt, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<false, false>), gt, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
