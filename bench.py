@@ -235,6 +235,7 @@ def backward_main(args, cfg, path):
                    "B": cfg.B, "H": cfg.H, "N": cfg.n_real, "d": cfg.d, "mode": cfg.mode,
                    "recipe": cfg.recipe, "algorithmic_flops": flops,
                    "backward_ms": round(ms_call, 4),
+                   "backward_ms_median": round(float(np.median(ms)), 4),
                    "backward_ms_min_max": [round(min(ms), 4), round(max(ms), 4)]},
         "roofline": {"bound": "mfma", "kernel": "whole backward call (prep, dK/dV, dQ)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
@@ -373,6 +374,7 @@ def main():
                    "dense_equivalent_flops": dense_equiv,
                    "quantize_ms": round(float(np.mean(q_ms)), 4),
                    "attention_ms": round(att_ms, 4),
+                   "attention_ms_median": round(float(np.median(a_ms)), 4),
                    "attention_ms_min_max": [round(min(a_ms), 4), round(max(a_ms), 4)],
                    "attention_tflops": round(achieved, 2),
                    "pct_fp8_peak": round(100 * achieved / PEAK_FP8, 2),
