@@ -183,7 +183,8 @@ __device__ inline float swap_sum(float v) {
 }
 __device__ inline float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// MODE: 0 dense, 1 causal (top-left aligned), 2 sliding-tile.
+// MODE: 0 dense, 1 causal (top-left aligned), 2 sliding-tile, 3 dense over
+// listed key tiles.
 // UK: the K scale is constant over each key tile (FP8 blocks a multiple of BN).
 //
 // Software pipeline over key tiles t = 0, 1, ...: iteration t
@@ -462,8 +463,9 @@ __global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
   // iteration's product with the zero P adds nothing.
   // Copies run up to three tiles past the last one.  Dense and causal tiles
   // past the end read zeros or in-bounds bytes of the same head (buffer
-  // loads check their range) into stages that are never read; sliding-tile
-  // steps repeat the last tile, since the window list ends there.
+  // loads check their range) into stages that are never read; list-driven
+  // steps (sliding-tile windows, listed key tiles) repeat the last listed
+  // tile, since the list ends there.
   auto tile_at = [&](int t) { return MODE >= 2 ? step_start(min(t, n_steps - 1)) : t * kBN; };
   issue_k<D, MX>(k0, hb, tile_at(0), wave, lane, kp);
   issue_aux<D, MX>(x0, hb, tile_at(0), lane);
@@ -801,7 +803,9 @@ __global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong variant for dense and causal attention with d = 128.
+// Ping-pong variant for dense attention with d = 128, over all key tiles or
+// the listed ones (mode 3).  It also handles the causal mask, which the
+// dispatch gives to the 4-wave kernel (faster there).
 //
 // A workgroup of 8 waves owns 256 queries of one head (32 per wave).  Waves w
 // and w + 4 share a SIMD; they form two groups that alternate between a
