@@ -129,12 +129,13 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
     p[i] = v;
 }
 
-// amax over a chunk of 256 tokens per workgroup; atomic max on the float bits
+// amax over a chunk of 512 tokens per workgroup (one round of resident
+// workgroups at 16K tokens x 40 heads); atomic max on the float bits
 // (valid for non-negative floats) into the scale buffer, which holds amax
 // until channel_finalize turns it into the scale.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void channel_amax_kernel(QuantArgs a) {
-  constexpr int TPR = D / 8, RPP = 256 / TPR, CHUNK = 256, ROUND = 256;
+  constexpr int TPR = D / 8, RPP = 256 / TPR, CHUNK = 512, ROUND = 256;
   const int bh = blockIdx.y, tid = threadIdx.x, col = (tid % TPR) * 8, r0 = tid / TPR;
   const int t0 = blockIdx.x * CHUNK;
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -358,7 +359,7 @@ static hipError_t launch_channel(const QuantArgs& a, hipStream_t st) {
   const int64_t ns = (int64_t)a.B * a.H * D;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<uint32_t*>(a.scales_f32), ns, 0u);
-  hipLaunchKernelGGL((channel_amax_kernel<T, D>), dim3((unsigned)((a.n_out + 255) / 256), a.B * a.H),
+  hipLaunchKernelGGL((channel_amax_kernel<T, D>), dim3((unsigned)((a.n_out + 511) / 512), a.B * a.H),
                      dim3(256), 0, st, a);
   hipLaunchKernelGGL((channel_encode_kernel<T, D>), dim3((unsigned)(a.n_alloc / 128), a.B * a.H),
                      dim3(256), 0, st, a);
