@@ -46,3 +46,52 @@ def attention(q, k, v, recipe="fp8", block_tokens=128, causal=False, sm_scale=No
         if bad:
             raise FloatingPointError("attention output holds %d non-finite values" % bad)
     return out
+
+
+def _attention_function():
+    import torch
+
+    class QuantizedAttention(torch.autograd.Function):
+        """Dense or causal attention on quantised operands with the gradient of
+        pab_attention_backward: the quantisers pass gradients straight through
+        (training-aware quantisation, the FPSAttention page's introduction).
+        The forward keeps the quantised operands, O and the row statistic for
+        the backward; d = 128."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, recipe, block_tokens, causal, sm_scale):
+            qq, kq, vq = quantize_qkv(q, k, v, recipe, block_tokens)
+            out, lse = B.attention_dense(qq, kq, vq, causal=causal, sm_scale=sm_scale, lse=True)
+            ctx.ops = (qq, kq, vq)
+            ctx.causal, ctx.sm_scale = causal, sm_scale
+            ctx.dtypes = (q.dtype, k.dtype, v.dtype)
+            ctx.save_for_backward(out, lse)
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            out, lse = ctx.saved_tensors
+            if dout.dtype not in (torch.float32, torch.bfloat16):
+                dout = dout.float()
+            if dout.stride(-1) != 1:
+                dout = dout.contiguous()
+            dq, dk, dv = B.attention_backward(*ctx.ops, out, dout, lse, causal=ctx.causal,
+                                              sm_scale=ctx.sm_scale)
+            dq, dk, dv = (g.to(t) for g, t in zip((dq, dk, dv), ctx.dtypes))
+            return dq, dk, dv, None, None, None, None
+
+    return QuantizedAttention
+
+
+_QA = None
+
+
+def attention_autograd(q, k, v, recipe="fp8", block_tokens=128, causal=False, sm_scale=None):
+    """attention() as a differentiable op for training: q, k, v CUDA tensors
+    [B, H, N, 128] (float32 or bfloat16); the backward runs
+    pab_attention_backward (gradients with respect to the dequantised
+    operands, passed straight through the quantisers)."""
+    global _QA
+    if _QA is None:
+        _QA = _attention_function()
+    return _QA.apply(q, k, v, recipe, block_tokens, causal, sm_scale)

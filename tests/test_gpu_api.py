@@ -61,3 +61,24 @@ def test_check_finite_raises(gpu_lib, monkeypatch):
     monkeypatch.setattr(api.B, "count_nonfinite", lambda out: torch.ones(1, dtype=torch.int32))
     with pytest.raises(FloatingPointError):
         api.attention(q, k, v, check_finite=True)
+
+
+@pytest.mark.parametrize("recipe,causal", [("fp8", True), ("mxfp4", False)])
+def test_autograd_uses_the_library_backward(gpu_lib, recipe, causal):
+    """attention_autograd's gradients are exactly those of a direct
+    pab_attention_backward call on the same quantised operands."""
+    from precision_attention_block_amd import api
+    rng = np.random.default_rng(80)
+    B, H, N, d = 1, 2, 300, 128
+    q, k, v = (torch.from_numpy(rng.standard_normal((B, H, N, d)).astype(np.float32)).to(torch.bfloat16)
+               .cuda().requires_grad_() for _ in range(3))
+    dout = torch.from_numpy(rng.standard_normal((B, H, N, d)).astype(np.float32)).cuda()
+    out = api.attention_autograd(q, k, v, recipe=recipe, block_tokens=64, causal=causal)
+    out.backward(dout)
+    qq, kq, vq = api.quantize_qkv(q.detach(), k.detach(), v.detach(), recipe, 64)
+    o2, lse = gpu_lib.attention_dense(qq, kq, vq, causal=causal, lse=True)
+    grads = gpu_lib.attention_backward(qq, kq, vq, o2, dout, lse, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2)
+    for g, ref in zip((q.grad, k.grad, v.grad), grads):
+        assert g.dtype == torch.bfloat16 and torch.equal(g, ref.to(torch.bfloat16))
