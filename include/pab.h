@@ -24,6 +24,17 @@
  *  - All arguments are validated before any launch; a call that returns an
  *    error other than PAB_HIP_ERROR has written nothing.
  *  - Element counts and strides are in elements, not bytes.
+ *  - Empty inputs: pab_quantize with B, H or n_out equal to 0, and
+ *    pab_attention_dense / pab_attention_backward with B, H or N equal to 0
+ *    (the three views agreeing on their sizes), return PAB_OK, launch
+ *    nothing and do not examine their pointers, which may be NULL.
+ *    Negative sizes are PAB_INVALID_ARG.  The sliding-tile calls need a
+ *    plan, which always holds tokens.
+ *  - Size limits (PAB_UNSUPPORTED beyond them), from the device's grid limits
+ *    and the kernels' 32-bit buffer offsets: pab_quantize B*H <= 65536,
+ *    n_out <= 2^27 and N_in < 2^31; the attention calls N <= 2^22,
+ *    B*H <= 2^24 and B*H*pab_token_alloc(N) < 2^31; the backward N <= 2^20
+ *    and B*H <= 65536.  Larger batches are split by the caller.
  *  - Quantised token buffers are padded: a tensor with n tokens is stored with
  *    n_alloc = pab_token_alloc(n) token slots (a multiple of PAB_TOKEN_ALIGN);
  *    the quantizers write zero codes into slots n..n_alloc-1.
@@ -39,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PAB_ABI_VERSION 5
+#define PAB_ABI_VERSION 6
 #define PAB_TOKEN_ALIGN 128  /* query tile of the attention kernel */
 #define PAB_MAX_TAU 8        /* largest softmax rescale threshold (log2 units) */
 
@@ -295,7 +306,9 @@ pab_status pab_sta_steps(const int32_t* win_off, const int32_t* win_idx, int n_t
  *           aligned, owned by the caller; contents on entry do not matter.
  * P, dS and dO enter their matrix products rounded to bf16; sums are fp32.
  * Strides must be multiples of 4 (float32) or 8 (bf16) elements and the
- * pointers 16-byte aligned.  PAB_UNSUPPORTED for d != 128 or N > 2^20.
+ * pointers 16-byte aligned.  PAB_UNSUPPORTED for d != 128, N > 2^20 or
+ * B*H > 65536.
+ * The workspace size is 0 for an empty input and -1 for a negative size.
  */
 int64_t pab_attention_backward_workspace(int64_t B, int64_t H, int64_t N, int64_t d);
 pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const pab_qview* v,

@@ -38,11 +38,21 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t round_up(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
 
+// Size limits.  They keep every launch inside the device's grid limits (fewer
+// than 2^32 work-items along a grid dimension, at most 65536 workgroups along
+// y) and every per-head buffer descriptor of the attention kernels below 2^31
+// bytes (the descriptors take 32-bit byte counts and offsets).
+constexpr int64_t kMaxAttnTokens = (int64_t)1 << 22;   // N per head: bf16 K operand, n_alloc * 256 B
+constexpr int64_t kMaxAttnRows = (int64_t)1 << 31;     // B*H*n_alloc (exclusive): 2 work-items per token slot
+constexpr int64_t kMaxGridY = 65536;                   // B*H of the quantiser and backward grids (y)
+constexpr int64_t kMaxQuantTokens = (int64_t)1 << 27;  // n_out: up to 16 work-items per token slot
+
 // Validates a quantised operand view; `role` 0 = Q/K, 1 = V.
 pab_status check_view(const pab_qview* v, int role) {
   if (!v || !v->codes || !v->scales) return PAB_INVALID_ARG;
   if (v->B < 1 || v->H < 1 || v->N < 1 || v->d < 1) return PAB_INVALID_ARG;
-  if (v->B * v->H > (int64_t)1 << 24 || v->N > (int64_t)1 << 28) return PAB_UNSUPPORTED;
+  if (v->B * v->H > (int64_t)1 << 24 || v->N > kMaxAttnTokens) return PAB_UNSUPPORTED;
+  if (v->B * v->H * round_up(v->N, PAB_TOKEN_ALIGN) >= kMaxAttnRows) return PAB_UNSUPPORTED;
   if (!aligned(v->codes, 16)) return PAB_INVALID_ARG;
   if (role == 1) {
     if (v->recipe == PAB_MXFP4_V) return v->d == 128 ? PAB_OK : PAB_UNSUPPORTED;
@@ -58,6 +68,19 @@ pab_status check_view(const pab_qview* v, int role) {
   }
   if (v->recipe == PAB_MXFP4_D32) return v->d == 128 ? PAB_OK : PAB_UNSUPPORTED;
   return PAB_INVALID_ARG;
+}
+
+// True for a call with nothing to compute: the three views agree on
+// (B, H, N, d), no size is negative and B, H or N is 0.  Such a call reads and
+// writes nothing, so its pointers are not examined.
+bool empty_views(const pab_qview* q, const pab_qview* k, const pab_qview* v) {
+  if (!q || !k || !v) return false;
+  for (const pab_qview* x : {q, k, v})
+    if (x->B < 0 || x->H < 0 || x->N < 0 || x->d < 1) return false;
+  if (q->B != k->B || q->B != v->B || q->H != k->H || q->H != v->H || q->N != k->N ||
+      q->N != v->N || q->d != k->d || q->d != v->d)
+    return false;
+  return q->B == 0 || q->H == 0 || q->N == 0;
 }
 
 pab_status fill_attn_args(const pab_qview* q, const pab_qview* k, const pab_qview* v,
@@ -165,7 +188,14 @@ pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
                         const int64_t strides[4], pab_recipe recipe, int block_tokens,
                         const int32_t* perm, int64_t n_out, void* codes, void* scales,
                         void* operand, void* stream) {
-  if (!x || !shape || !strides || !codes || !scales) return PAB_INVALID_ARG;
+  if (!shape || !strides) return PAB_INVALID_ARG;
+  {
+    const int64_t B = shape[0], H = shape[1], N = shape[2], d = shape[3];
+    if (B < 0 || H < 0 || N < 0 || d < 1 || n_out < 0) return PAB_INVALID_ARG;
+    if (!perm && n_out != N) return PAB_INVALID_ARG;
+    if (B == 0 || H == 0 || n_out == 0) return PAB_OK;   // empty output: nothing to do
+  }
+  if (!x || !codes || !scales) return PAB_INVALID_ARG;
   if (operand && (recipe != PAB_FP8_TOKEN_BLOCK || !aligned(operand, 16))) return PAB_INVALID_ARG;
   if (in_dt != PAB_F32 && in_dt != PAB_BF16) return PAB_INVALID_ARG;
   const int64_t B = shape[0], H = shape[1], N = shape[2], d = shape[3];
@@ -176,7 +206,7 @@ pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return PAB_INVALID_ARG;
   if (n_out < 1) return PAB_INVALID_ARG;
   if (!perm && n_out != N) return PAB_INVALID_ARG;
-  if (B * H > (int64_t)1 << 24 || n_out > (int64_t)1 << 28 || N > (int64_t)1 << 31) return PAB_UNSUPPORTED;
+  if (B * H > kMaxGridY || n_out > kMaxQuantTokens || N > INT32_MAX) return PAB_UNSUPPORTED;
   if (recipe == PAB_FP8_TOKEN_BLOCK) {
     if (d != 64 && d != 128) return PAB_UNSUPPORTED;
     if (block_tokens < 16 || block_tokens > 16384 || block_tokens % 16) return PAB_INVALID_ARG;
@@ -221,6 +251,7 @@ pab_status pab_attention_dense(const pab_qview* q, const pab_qview* k, const pab
                                int causal, float sm_scale, int tau, const uint8_t* kv_valid,
                                const int32_t* out_perm, int64_t n_out_tokens, float* out,
                                const int64_t out_strides[4], float* lse, void* stream) {
+  if (empty_views(q, k, v) && n_out_tokens >= 0) return PAB_OK;
   pab::AttnArgs a;
   pab_status s = fill_attn_args(q, k, v, sm_scale, tau, kv_valid, out_perm, n_out_tokens, out,
                                 out_strides, a);
@@ -360,7 +391,8 @@ pab_status pab_sta_steps(const int32_t* win_off, const int32_t* win_idx, int n_t
 }
 
 int64_t pab_attention_backward_workspace(int64_t B, int64_t H, int64_t N, int64_t d) {
-  if (B < 1 || H < 1 || N < 1 || d < 1) return -1;
+  if (B < 0 || H < 0 || N < 0 || d < 1) return -1;
+  if (B == 0 || H == 0 || N == 0) return 0;
   int64_t off[13];
   return pab::bwd_workspace_layout(B * H, round_up(N, PAB_TOKEN_ALIGN), d, off);
 }
@@ -372,6 +404,7 @@ pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const 
                                   const int64_t dout_strides[4], const float* lse, float* dq,
                                   float* dk, float* dv, const int64_t grad_strides[4],
                                   void* workspace, int64_t workspace_bytes, void* stream) {
+  if (empty_views(q, k, v)) return PAB_OK;
   pab_status s;
   if ((s = check_view(q, 0)) != PAB_OK) return s;
   if ((s = check_view(k, 0)) != PAB_OK) return s;
@@ -380,7 +413,7 @@ pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const 
   if (q->B != k->B || q->B != v->B || q->H != k->H || q->H != v->H || q->N != k->N ||
       q->N != v->N || q->d != k->d || q->d != v->d)
     return PAB_INVALID_ARG;
-  if (q->d != 128 || q->N > ((int64_t)1 << 20)) return PAB_UNSUPPORTED;
+  if (q->d != 128 || q->N > ((int64_t)1 << 20) || q->B * q->H > kMaxGridY) return PAB_UNSUPPORTED;
   if (dout_dtype != PAB_F32 && dout_dtype != PAB_BF16) return PAB_INVALID_ARG;
   if (!out || !out_strides || !dout || !dout_strides || !lse || !dq || !dk || !dv ||
       !grad_strides || !workspace)

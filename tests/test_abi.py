@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(B):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(B.lib(), name), name
-    assert B.lib().pab_abi_version() == 5
+    assert B.lib().pab_abi_version() == 6
 
 
 def test_token_alloc_and_info(B):
@@ -142,7 +142,8 @@ def test_backward_validation_without_device(B):
     need = L.pab_attention_backward_workspace(1, 2, 256, 128)
     # seven bf16 [BH, n_alloc, d] arrays, four float32 [BH, n_alloc], one float32 [n_alloc]
     assert need == 7 * 2 * 256 * 128 * 2 + 4 * 2 * 256 * 4 + 256 * 4
-    assert L.pab_attention_backward_workspace(0, 2, 256, 128) < 0
+    assert L.pab_attention_backward_workspace(0, 2, 256, 128) == 0      # empty
+    assert L.pab_attention_backward_workspace(-1, 2, 256, 128) < 0
 
     def bwd(q=qv, k=kv, v=vv, ws=fake * 16, nbytes=need, dt=B.PAB_F32, lse=f, gstr=st, dstr=st):
         return L.pab_attention_backward(
@@ -224,3 +225,73 @@ def test_planner_validation(B):
     assert L.pab_sta_plan(c3((12, 48, 80)), c3((13, 48, 80)), c3((6, 8, 8)), c3((3, 3, 3)),
                           None, None, None, None, None, None, ctypes.byref(n), None, None) \
         == B.PAB_INVALID_ARG                                  # real grid larger than grid
+
+
+def test_empty_inputs_are_no_ops_without_device(B):
+    """B, H or N equal to 0: OK with NULL pointers, nothing launched (the calls
+    would fault on a NULL pointer otherwise); negative sizes are invalid."""
+    L = B.lib()
+    null = ctypes.c_void_p(0)
+    st = B._i64([0, 0, 0, 1])
+    for shape, n_out in (([1, 2, 0, 128], 0), ([0, 2, 256, 128], 256), ([1, 0, 256, 128], 256)):
+        assert L.pab_quantize(null, 1, B._i64(shape), st, 0, 128, null, n_out, null, null, null,
+                              null) == B.PAB_OK
+    assert L.pab_quantize(null, 1, B._i64([1, 2, 0, 128]), st, 0, 128, null, 5, null, null, null,
+                          null) == B.PAB_INVALID_ARG                  # n_out != N without perm
+    assert L.pab_quantize(null, 1, B._i64([1, -1, 4, 128]), st, 0, 128, null, 4, null, null, null,
+                          null) == B.PAB_INVALID_ARG
+    mk = lambda recipe, B_=1, H=2, n=0: B.QView(0, 0, 0, recipe, 128, B_, H, n, 128)
+    out_str = B._i64([0, 0, 128, 1])
+    for b_, h, n in ((1, 2, 0), (0, 2, 256), (1, 0, 256)):
+        q, k, v = mk(0, b_, h, n), mk(0, b_, h, n), mk(1, b_, h, n)
+        assert L.pab_attention_dense(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 1, 0.0, 0,
+                                     null, null, n, null, out_str, null, null) == B.PAB_OK
+        assert L.pab_attention_backward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, 0.0,
+                                        null, null, out_str, null, 0, out_str, null, null, null,
+                                        null, out_str, null, 0, null) == B.PAB_OK
+        assert B.backward_workspace_bytes(b_, h, n, 128) == 0
+    q, k, v = mk(0, n=0), mk(0, n=4), mk(1, n=0)           # sizes disagree: not an empty call
+    assert L.pab_attention_dense(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, 0.0, 0, null,
+                                 null, 0, null, out_str, null, null) == B.PAB_INVALID_ARG
+    q = mk(0, n=-1)
+    assert L.pab_attention_dense(ctypes.byref(q), ctypes.byref(q), ctypes.byref(mk(1, n=-1)), 0, 0.0,
+                                 0, null, null, 0, null, out_str, null, null) == B.PAB_INVALID_ARG
+    assert B.backward_workspace_bytes(1, 2, -1, 128) == -1
+    assert L.pab_last_hip_error() == 0
+
+
+def test_size_limits_without_device(B):
+    """Sizes past the device's grid limits or the kernels' 32-bit buffer
+    offsets are PAB_UNSUPPORTED before any launch; the largest allowed sizes
+    pass validation (checked with a NULL output, which is then rejected)."""
+    L = B.lib()
+    fake = ctypes.c_void_p(4096)
+    null = ctypes.c_void_p(0)
+
+    def quant(b, h, n, blk=128):
+        return L.pab_quantize(fake, 1, B._i64([b, h, n, 128]), B._i64([0, 0, 128, 1]), 0, blk, null,
+                              n, fake, fake, fake, null)
+    # every call here fails validation: block 100 is invalid, checked after the limits
+    assert quant(1, 65537, 128, blk=100) == B.PAB_UNSUPPORTED        # grid y
+    assert quant(1, 65536, 128, blk=100) == B.PAB_INVALID_ARG
+    assert quant(1, 1, (1 << 27) + 1, blk=100) == B.PAB_UNSUPPORTED
+    assert quant(1, 1, 1 << 27, blk=100) == B.PAB_INVALID_ARG
+    assert quant(1, 1, 1 << 31) == B.PAB_UNSUPPORTED
+
+    def dense(b, h, n, out=fake):
+        mk = lambda recipe: B.QView(4096, 4096, 4096, recipe, 128, b, h, n, 128)
+        q, k, v = mk(0), mk(0), mk(1)
+        return L.pab_attention_dense(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, 0.0, 0,
+                                     null, null, n, out, B._i64([0, 0, 128, 1]), null, null)
+    assert dense(1, 1, (1 << 22) + 1) == B.PAB_UNSUPPORTED           # per-head descriptor bytes
+    assert dense(1, 1, 1 << 22, out=null) == B.PAB_INVALID_ARG       # allowed size, NULL output
+    assert dense(1 << 9, 1, 1 << 22) == B.PAB_UNSUPPORTED            # B*H*n_alloc = 2^31
+    assert dense(1, (1 << 9) - 1, 1 << 22, out=null) == B.PAB_INVALID_ARG
+    assert dense(1, (1 << 24) + 1, 128) == B.PAB_UNSUPPORTED
+    mk = lambda recipe: B.QView(4096, 4096, 4096, recipe, 128, 1, 65537, 256, 128)
+    q, k, v = mk(0), mk(0), mk(1)
+    st = B._i64([0, 0, 128, 1])
+    assert L.pab_attention_backward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, 0.0, null,
+                                    fake, st, fake, 0, st, fake, fake, fake, fake, st,
+                                    ctypes.c_void_p(4096 * 256), 1 << 40, null) == B.PAB_UNSUPPORTED
+    assert L.pab_last_hip_error() == 0

@@ -82,3 +82,23 @@ def test_autograd_uses_the_library_backward(gpu_lib, recipe, causal):
     assert torch.equal(out, o2)
     for g, ref in zip((q.grad, k.grad, v.grad), grads):
         assert g.dtype == torch.bfloat16 and torch.equal(g, ref.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 0, 128), (0, 2, 256, 128), (1, 0, 256, 128)])
+@pytest.mark.parametrize("recipe", ["fp8", "mxfp4", "mxfp4_pv"])
+def test_empty_inputs(gpu_lib, shape, recipe):
+    """An empty batch, head or token axis gives empty outputs and gradients
+    (the library launches nothing), and the device stays usable."""
+    from precision_attention_block_amd import api
+    print("empty case", shape, recipe, flush=True)
+    q, k, v = (torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    out = api.attention(q, k, v, recipe=recipe, block_tokens=128)
+    assert out.shape == shape and out.dtype == torch.float32
+    qq, kq, vq = api.quantize_qkv(q, k, v, recipe, 128)
+    o, lse = gpu_lib.attention_dense(qq, kq, vq, causal=True, lse=True)
+    assert o.shape == shape and lse.shape == shape[:3]
+    grads = gpu_lib.attention_backward(qq, kq, vq, o, torch.zeros(shape, device="cuda"), lse)
+    assert all(g.shape == shape for g in grads)
+    torch.cuda.synchronize()
+    x = torch.randn(1, 1, 256, 128, device="cuda")
+    assert torch.all(torch.isfinite(api.attention(x, x, x)))
