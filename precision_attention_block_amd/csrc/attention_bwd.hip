@@ -17,9 +17,10 @@
 //
 // Two kernels, FlashAttention-2 style, so no atomics and a deterministic sum
 // order:
-//  * dK/dV: a workgroup owns 128 keys (4 waves x 32); each wave keeps the K
-//    and V rows of its keys in registers as B operands and walks the queries
-//    in steps of 32.
+//  * dK/dV: a workgroup owns 128 keys (4 blocks of 32, each split over a
+//    wave that keeps the K rows as B operands and forms P and dV, and a wave
+//    that keeps the V rows and forms dP, dS and dK) and walks the queries in
+//    steps of 32.
 //  * dQ: a workgroup owns 128 queries; each wave keeps the Q and dO rows of
 //    its queries in registers and walks the keys in steps of 32.
 // In the 32x32 MFMA result layout a lane holds one column and 16 rows
@@ -295,46 +296,71 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
 }
 
-// Packs registers 8h .. 8h+7 of a score tile into a bf16 B operand.
-__device__ inline v8s pack_b(const float (&x)[16], int h) {
-  return __builtin_bit_cast(v8s, make_uint4(bf16x2(x[8 * h], x[8 * h + 1]), bf16x2(x[8 * h + 2], x[8 * h + 3]),
-                                            bf16x2(x[8 * h + 4], x[8 * h + 5]),
-                                            bf16x2(x[8 * h + 6], x[8 * h + 7])));
-}
 #endif  // __HIP_DEVICE_COMPILE__
 
-// ---- dK, dV --------------------------------------------------------------------
+// ---- dK, dV ---------------------------------------------------------------------
+// A workgroup of 8 waves owns 128 keys and walks the queries in steps of 32.
+// Each 32-key block is split over two waves, so that each holds one operand
+// and one accumulator (about half the registers of one wave doing all four
+// products) and two waves share every SIMD:
+//  * P-wave (waves 0-3, key block w): K operand and the dV accumulator.  For
+//    step t+1 it forms S = Q K^T, P = 2^(S c - LSE) (masked), stores P (fp32)
+//    in an LDS exchange buffer and adds dV^T += dO^T P.
+//  * dS-wave (waves 4-7, key block w - 4): V operand and the dK accumulator.
+//    For step t it forms dP = (dO / s_V) V_codes^T, reads P of step t from the
+//    exchange buffer, dS' = P (dP - D) sm / s_Q (zero wherever P was masked)
+//    and adds dK^T += Q_vals^T dS'.
+// Waves w and w + 4 run on the same SIMD.  Three LDS stages hold steps t,
+// t+1 (read) and t+2 (being copied); the exchange buffer is double-buffered
+// by step parity.  One barrier per step orders the copies, the exchange and
+// the reuse of stages.
 // UQ: the Q block scale is the same for all 32 queries of a step (MXFP4, or
 // FP8 blocks of a multiple of 32 tokens), so one fma forms each exponent
 // argument and dS takes one fma and one multiply.
-template <bool CAUSAL, bool UQ>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __align__(16) uint8_t st0[Stage::BYTES], st1[Stage::BYTES], st2[Stage::BYTES];
+struct PairLds {
+  static constexpr int PX = 3 * Stage::BYTES;             // exchange buffers
+  static constexpr int PX_BYTES = 4 * 64 * 16 * 4;        // 4 key blocks x 64 lanes x 16 floats
+  static constexpr int BYTES = PX + 2 * PX_BYTES;
+};
+
+// One wave's share of a stage's copies with 8 waves: one instruction per tile
+// plus the per-token floats.
+__device__ inline void issue_stage8(uint8_t* stg, int q0, int wave, int lane,
+                                    __amdgpu_buffer_rsrc_t qr, __amdgpu_buffer_rsrc_t dr,
+                                    __amdgpu_buffer_rsrc_t qtr, __amdgpu_buffer_rsrc_t dtr,
+                                    __amdgpu_buffer_rsrc_t lsr, __amdgpu_buffer_rsrc_t ddr,
+                                    __amdgpu_buffer_rsrc_t fqr, const DmaPlan<16>& pr,
+                                    const DmaPlan<4>& pt) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void_t*)(stg + Stage::R0 + wave * 1024), 16,
+                                           pr.off[wave % 4], (q0 + 4 * wave) * 2 * kD, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void_t*)(stg + Stage::R1 + wave * 1024), 16,
+                                           pr.off[wave % 4], (q0 + 4 * wave) * 2 * kD, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(qtr, (lds_void_t*)(stg + Stage::T0 + wave * 1024), 16,
+                                           pt.off[0], q0 * 2 * kD + wave * 1024, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(dtr, (lds_void_t*)(stg + Stage::T1 + wave * 1024), 16,
+                                           pt.off[0], q0 * 2 * kD + wave * 1024, 0, 0);
+  issue_floats(lsr, stg + Stage::F0, q0, lane);
+  issue_floats(ddr, stg + Stage::F1, q0, lane);
+  issue_floats(fqr, stg + Stage::F2, q0, lane);
+}
+#endif  // __HIP_DEVICE_COMPILE__
+
+template <bool CAUSAL, bool UQ>
+__global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __align__(16) uint8_t lds[PairLds::BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pwave = wave < 4;
+  const int kblk = wave & 3;
   const int lr = lane & 31, lg = lane >> 5;
   const int n_kt = a.n_alloc / kBwdTile;
   const int work = xcd_work_index(blockIdx.x, gridDim.x);
   const int bh = work / n_kt, kt = work % n_kt;
-  const int key0 = kt * kBwdTile + 32 * wave;   // this wave's 32 keys
+  const int key0 = kt * kBwdTile + 32 * kblk;   // this wave's 32 keys
   const int j = key0 + lr;                      // this lane's key
   const int64_t tokb = (int64_t)bh * a.n_alloc;
-
-  // K and V rows of key j as B operands: k-step s holds channels 16 s + 8 lg .. + 7
-  v8s kb[8], vb[8];
-  {
-    const uint4* kr = reinterpret_cast<const uint4*>(a.k_rows + (tokb + j) * kD);
-    const uint4* vr = reinterpret_cast<const uint4*>(a.v_rows + (tokb + j) * kD);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kb[s] = __builtin_bit_cast(v8s, kr[2 * s + lg]);
-      vb[s] = __builtin_bit_cast(v8s, vr[2 * s + lg]);
-    }
-  }
-  const float ck = a.sm_log2 * a.fk[tokb + j];
-  const bool kvalid = a.kvf[j] != 0.0f;
-  const bool all_valid = __all(kvalid);
 
   const auto qr = rsrc(a.q_rows + tokb * kD, (int64_t)a.n_alloc * kD * 2);
   const auto dr = rsrc(a.dos_rows + tokb * kD, (int64_t)a.n_alloc * kD * 2);
@@ -346,150 +372,185 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   DmaPlan<16> pr;
   pr.init(lane, 2 * kD);
   DmaPlan<4> pt;
-  pt.init(lane, 64);   // transposed rows of one step are 64 bytes apart
-  auto issue = [&](uint8_t* stg, int q0) __attribute__((always_inline)) {
-    issue_rows(qr, stg + Stage::R0, q0, wave, pr);
-    issue_rows(dr, stg + Stage::R1, q0, wave, pr);
-    issue_trans(qtr, stg + Stage::T0, q0, wave, pt);
-    issue_trans(dtr, stg + Stage::T1, q0, wave, pt);
-    issue_floats(lsr, stg + Stage::F0, q0, lane);
-    issue_floats(ddr, stg + Stage::F1, q0, lane);
-    issue_floats(fqr, stg + Stage::F2, q0, lane);
+  pt.init(lane, 64);
+  auto stage = [&](int i) __attribute__((always_inline)) { return lds + (i % 3) * Stage::BYTES; };
+  // exchange slot of (step parity, this key block); lane l's 16 floats sit at
+  // 16-byte chunks k * 1024 + 16 l (k < 4), so every access is one
+  // contiguous KB per instruction
+  auto xch = [&](int t) __attribute__((always_inline)) {
+    return lds + PairLds::PX + (t & 1) * PairLds::PX_BYTES + kblk * 4096 + 16 * lane;
+  };
+  const int q_begin = CAUSAL ? kt * kBwdTile : 0;   // earlier queries see none of these keys
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    issue_stage8(stage(t), q_begin + 32 * t, wave, lane, qr, dr, qtr, dtr, lsr, ddr, fqr, pr, pt);
+  };
+  const int q_end = (a.N + 31) / 32 * 32;
+  const int n_steps = (q_end - q_begin) / 32;
+  constexpr int kIssues = 7;   // copy instructions per wave per stage
+
+  // lane (key j, lg) of an accumulator holds channels 32 cb + 8 i + 4 lg + r
+  auto store_rows = [&](float* base, const v16f (&acc)[4]) __attribute__((always_inline)) {
+    if (j >= a.N) return;
+    const int b = bh / a.H, h = bh % a.H;
+    float* row = base + b * a.g_sb + h * a.g_sh + (int64_t)j * a.g_sn;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(row + 32 * cb + 8 * i + 4 * lg) =
+            make_float4(acc[cb][4 * i], acc[cb][4 * i + 1], acc[cb][4 * i + 2], acc[cb][4 * i + 3]);
   };
 
-  v16f dvt[4], dkt[4];
+  if (pwave) {
+    v8s kb[8];
+    {
+      const uint4* kr = reinterpret_cast<const uint4*>(a.k_rows + (tokb + j) * kD);
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) dvt[cb][e] = dkt[cb][e] = 0.0f;
-
-  // S (queries x keys) = Q K^T and dP = (dO / s_V) V_codes^T of the step in
-  // stage `cur`.  Register 4 i + r of the score tiles is query q0 + 8 i +
-  // 4 lg + r.
-  auto products = [&](const uint8_t* cur, v16f& s, v16f& dp) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R0, lr, 2 * ks + lg), kb[ks], s,
-                                                  0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R1, lr, 2 * ks + lg), vb[ks],
-                                                   dp, 0, 0, 0);
+      for (int s = 0; s < 8; ++s) kb[s] = __builtin_bit_cast(v8s, kr[2 * s + lg]);
     }
-  };
-  // The rest of a step from its scores: P, dS and the dV / dK products.
-  auto finish = [&](const int q0, const uint8_t* cur, const v16f& s, const v16f& dp)
-      __attribute__((always_inline)) {
-    float cs = 0.0f, sc = 0.0f;
-    if (UQ) {
-      const float fq = *reinterpret_cast<const float*>(cur + Stage::F2);
-      cs = ck * fq;        // exponent argument: S cs - LSE
-      sc = a.sm * fq;      // dS scaled for dK^ = sm dS^T Q^
-    }
-    const bool masked = !all_valid || (CAUSAL && q0 < key0 + 32);
-    // P = 2^(S c - LSE), dS' = P (dP - D) sm / s_Q, packed per half h into
-    // the bf16 B operands of the products over queries 16 h .. 16 h + 15.
-    // Masked steps keep register 4 i + r only if 8 i + r >= thr (query >= key
-    // for causal masks; never for a masked key).
-    const int thr = !kvalid ? 64 : CAUSAL ? j - q0 - 4 * lg : -64;
-    v8s pb[2], db[2];
+    const float ck = a.sm_log2 * a.fk[tokb + j];
+    const bool kvalid = a.kvf[j] != 0.0f;
+    const bool all_valid = __all(kvalid);
+    v16f dvt[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float p[8], ds[8];
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * h + ii;
+      for (int e = 0; e < 16; ++e) dvt[cb][e] = 0.0f;
+    // S, P and dV of step t (stage t % 3); P goes to exchange slot t & 1
+    auto pstep = [&](const int t) __attribute__((always_inline)) {
+      const uint8_t* cur = stage(t);
+      const int q0 = q_begin + 32 * t;
+      v16f s;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R0, lr, 2 * ks + lg), kb[ks],
+                                                    s, 0, 0, 0);
+      float cs = 0.0f;
+      if (UQ) cs = ck * *reinterpret_cast<const float*>(cur + Stage::F2);
+      const bool masked = !all_valid || (CAUSAL && q0 < key0 + 32);
+      // register 4 i + r is query q0 + 8 i + 4 lg + r; masked steps keep it
+      // only if 8 i + r >= thr (query >= key for causal masks; never for a
+      // masked key)
+      const int thr = !kvalid ? 64 : CAUSAL ? j - q0 - 4 * lg : -64;
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         const float4 l4 = *reinterpret_cast<const float4*>(cur + Stage::F0 + 4 * (8 * i + 4 * lg));
-        const float4 d4 = *reinterpret_cast<const float4*>(cur + Stage::F1 + 4 * (8 * i + 4 * lg));
         float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
         if (!UQ) f4 = *reinterpret_cast<const float4*>(cur + Stage::F2 + 4 * (8 * i + 4 * lg));
-        const float lse[4] = {l4.x, l4.y, l4.z, l4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
-        const float fq[4] = {f4.x, f4.y, f4.z, f4.w};
+        const float lse[4] = {l4.x, l4.y, l4.z, l4.w}, fq[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = 4 * i + r;
-          const float pe = __builtin_amdgcn_exp2f(UQ ? fmaf(s[e], cs, -lse[r]) : fmaf(s[e] * ck, fq[r], -lse[r]));
-          p[4 * ii + r] = pe;
-          ds[4 * ii + r] = UQ ? pe * fmaf(dp[e], sc, -dd[r] * sc) : pe * (dp[e] - dd[r]) * (a.sm * fq[r]);
+          p[e] = __builtin_amdgcn_exp2f(UQ ? fmaf(s[e], cs, -lse[r]) : fmaf(s[e] * ck, fq[r], -lse[r]));
         }
       }
       if (masked) {
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const bool keep = 8 * (2 * h + x / 4) + x % 4 >= thr;
-          p[x] = keep ? p[x] : 0.0f;
-          ds[x] = keep ? ds[x] : 0.0f;
-        }
+        for (int e = 0; e < 16; ++e) p[e] = 8 * (e / 4) + e % 4 >= thr ? p[e] : 0.0f;
       }
-      pb[h] = __builtin_bit_cast(v8s, make_uint4(bf16x2(p[0], p[1]), bf16x2(p[2], p[3]),
-                                                 bf16x2(p[4], p[5]), bf16x2(p[6], p[7])));
-      db[h] = __builtin_bit_cast(v8s, make_uint4(bf16x2(ds[0], ds[1]), bf16x2(ds[2], ds[3]),
-                                                 bf16x2(ds[4], ds[5]), bf16x2(ds[6], ds[7])));
+      uint8_t* x = xch(t);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<float4*>(x + k * 1024) = make_float4(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]);
+      v8s pb[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        pb[h] = __builtin_bit_cast(v8s, make_uint4(bf16x2(p[8 * h], p[8 * h + 1]), bf16x2(p[8 * h + 2], p[8 * h + 3]),
+                                                   bf16x2(p[8 * h + 4], p[8 * h + 5]),
+                                                   bf16x2(p[8 * h + 6], p[8 * h + 7])));
+      // dV^T += dO^T P (channels x keys, K = queries)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          dvt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_t_operand(cur + Stage::T1, 32 * cb + lr, 2 * h + lg), pb[h], dvt[cb], 0, 0, 0);
+    };
+    issue(0);
+    issue(1);
+    wait_vm_le<kIssues>();
+    barrier_lds();
+    if (n_steps > 0) pstep(0);
+    for (int t = 0; t + 1 < n_steps; ++t) {
+      wait_vm_le<0>();
+      barrier_lds();   // step t+1 has landed; stage (t+2) % 3 and slot (t+1) & 1 are free
+      issue(t + 2);
+      pstep(t + 1);
     }
-    // dV^T += dO^T P and dK^T += Q_vals^T dS' (channels x keys, K = queries)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int row = 32 * cb + lr;
-        dvt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T1, row, 2 * h + lg), pb[h],
-                                                          dvt[cb], 0, 0, 0);
-        dkt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T0, row, 2 * h + lg), db[h],
-                                                          dkt[cb], 0, 0, 0);
-      }
-  };
-
-  const int q_begin = CAUSAL ? kt * kBwdTile : 0;   // earlier queries see none of these keys
-  const int q_end = (a.N + 31) / 32 * 32;
-  // Steps wholly above the diagonal (causal) are computed and masked rather
-  // than skipped: a branch around the products makes the compiler move every
-  // accumulator between register files on each step, and such steps are at
-  // most three per workgroup.
-  // Software pipeline over 32-query steps t (three LDS stages): iteration t
-  // copies step t+2, forms the scores of step t+1 while the vector unit works
-  // on step t, then adds step t's products.  The body has no branch, so the
-  // compiler can interleave the matrix and vector work; past the last step
-  // the copies and score products run on data that is never used (the
-  // buffer descriptors bound every copy).
-  const int n_steps = (q_end - q_begin) / 32;
-  auto stage = [&](int i) __attribute__((always_inline)) { return i == 0 ? st0 : i == 1 ? st1 : st2; };
-  issue(st0, q_begin);
-  issue(st1, q_begin + 32);
-  constexpr int kIssues = 11;   // copy instructions per wave per stage
-  wait_vm_le<kIssues>();
-  barrier_lds();
-  v16f sa, dpa, sb, dpb;
-  products(st0, sa, dpa);
-  auto body = [&](const int t, v16f& s_cur, v16f& dp_cur, v16f& s_nxt, v16f& dp_nxt)
-      __attribute__((always_inline)) {
     wait_vm_le<0>();
-    barrier_lds();   // step t+1 has landed everywhere; stage (t+2) % 3 is free
-    issue(stage((t + 2) % 3), q_begin + 32 * (t + 2));
-    products(stage((t + 1) % 3), s_nxt, dp_nxt);
-    finish(q_begin + 32 * t, stage(t % 3), s_cur, dp_cur);
-  };
-  int t = 0;
-  for (; t + 2 <= n_steps; t += 2) {
-    body(t, sa, dpa, sb, dpb);
-    body(t + 1, sb, dpb, sa, dpa);
-  }
-  if (t < n_steps) finish(q_begin + 32 * t, stage(t % 3), sa, dpa);   // odd count: the last step
-  wait_vm_le<0>();   // no copy may still target this workgroup's LDS when it ends
-  // lane (key j, lg) holds channels 32 cb + 8 i + 4 lg + r
-  if (j < a.N) {
-    const int b = bh / a.H, h = bh % a.H;
-    float* dvrow = a.dv + b * a.g_sb + h * a.g_sh + (int64_t)j * a.g_sn;
-    float* dkrow = a.dk + b * a.g_sb + h * a.g_sh + (int64_t)j * a.g_sn;
+    barrier_lds();     // the dS-waves' last step
+    issue(n_steps + 1);
+    wait_vm_le<0>();   // no copy may still target this workgroup's LDS when it ends
+    store_rows(a.dv, dvt);
+  } else {
+    v8s vb[8];
+    {
+      const uint4* vr = reinterpret_cast<const uint4*>(a.v_rows + (tokb + j) * kD);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) vb[s] = __builtin_bit_cast(v8s, vr[2 * s + lg]);
+    }
+    v16f dkt[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
+      for (int e = 0; e < 16; ++e) dkt[cb][e] = 0.0f;
+    // dP, dS and dK of step t
+    auto dstep = [&](const int t) __attribute__((always_inline)) {
+      const uint8_t* cur = stage(t);
+      v16f dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dp[e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R1, lr, 2 * ks + lg), vb[ks],
+                                                     dp, 0, 0, 0);
+      float sc = 0.0f;
+      if (UQ) sc = a.sm * *reinterpret_cast<const float*>(cur + Stage::F2);
+      const uint8_t* x = xch(t);
+      float ds[16];
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c0 = 32 * cb + 8 * i + 4 * lg;
-        *reinterpret_cast<float4*>(dvrow + c0) =
-            make_float4(dvt[cb][4 * i], dvt[cb][4 * i + 1], dvt[cb][4 * i + 2], dvt[cb][4 * i + 3]);
-        *reinterpret_cast<float4*>(dkrow + c0) =
-            make_float4(dkt[cb][4 * i], dkt[cb][4 * i + 1], dkt[cb][4 * i + 2], dkt[cb][4 * i + 3]);
+        const float4 p4 = *reinterpret_cast<const float4*>(x + i * 1024);
+        const float4 d4 = *reinterpret_cast<const float4*>(cur + Stage::F1 + 4 * (8 * i + 4 * lg));
+        float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (!UQ) f4 = *reinterpret_cast<const float4*>(cur + Stage::F2 + 4 * (8 * i + 4 * lg));
+        const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float fq[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * i + r;
+          ds[e] = UQ ? pv[r] * fmaf(dp[e], sc, -dd[r] * sc) : pv[r] * (dp[e] - dd[r]) * (a.sm * fq[r]);
+        }
       }
+      v8s db[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        db[h] = __builtin_bit_cast(v8s, make_uint4(bf16x2(ds[8 * h], ds[8 * h + 1]), bf16x2(ds[8 * h + 2], ds[8 * h + 3]),
+                                                   bf16x2(ds[8 * h + 4], ds[8 * h + 5]),
+                                                   bf16x2(ds[8 * h + 6], ds[8 * h + 7])));
+      // dK^T += Q_vals^T dS' (channels x keys, K = queries)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          dkt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_t_operand(cur + Stage::T0, 32 * cb + lr, 2 * h + lg), db[h], dkt[cb], 0, 0, 0);
+    };
+    issue(0);
+    issue(1);
+    wait_vm_le<kIssues>();
+    barrier_lds();
+    for (int t = 0; t < n_steps; ++t) {
+      wait_vm_le<0>();
+      barrier_lds();   // P of step t is in its slot; stage (t+2) % 3 is free
+      issue(t + 2);
+      dstep(t);
+    }
+    wait_vm_le<0>();
+    store_rows(a.dk, dkt);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -670,18 +731,18 @@ hipError_t launch_attention_backward(const BwdArgs& a, hipStream_t st) {
   const bool uk = a.qk_mx || a.blk_k % 32 == 0;
   if (a.causal) {
     if (uq)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<true, true>), gt, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<true, true>), gt, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<true, false>), gt, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<true, false>), gt, dim3(512), 0, st, a);
     if (uk)
       hipLaunchKernelGGL((bwd_dq_kernel<true, true>), gt, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<true, false>), gt, dim3(256), 0, st, a);
   } else {
     if (uq)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<false, true>), gt, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<false, true>), gt, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<false, false>), gt, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<false, false>), gt, dim3(512), 0, st, a);
     if (uk)
       hipLaunchKernelGGL((bwd_dq_kernel<false, true>), gt, dim3(256), 0, st, a);
     else
