@@ -324,8 +324,8 @@ struct PairLds {
   static constexpr int BYTES = PX + 2 * PX_BYTES;
 };
 
-// One wave's share of a stage's copies with 8 waves: one instruction per tile
-// plus the per-token floats.
+// One wave's share of a stage's copies with 8 waves: one instruction per tile;
+// waves 0, 1 and 2 also copy the LSE, D and 1/s_Q floats of the step.
 __device__ inline void issue_stage8(uint8_t* stg, int q0, int wave, int lane,
                                     __amdgpu_buffer_rsrc_t qr, __amdgpu_buffer_rsrc_t dr,
                                     __amdgpu_buffer_rsrc_t qtr, __amdgpu_buffer_rsrc_t dtr,
@@ -340,9 +340,8 @@ __device__ inline void issue_stage8(uint8_t* stg, int q0, int wave, int lane,
                                            pt.off[0], q0 * 2 * kD + wave * 1024, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(dtr, (lds_void_t*)(stg + Stage::T1 + wave * 1024), 16,
                                            pt.off[0], q0 * 2 * kD + wave * 1024, 0, 0);
-  issue_floats(lsr, stg + Stage::F0, q0, lane);
-  issue_floats(ddr, stg + Stage::F1, q0, lane);
-  issue_floats(fqr, stg + Stage::F2, q0, lane);
+  if (wave < 3)
+    issue_floats(wave == 0 ? lsr : wave == 1 ? ddr : fqr, stg + Stage::F0 + 256 * wave, q0, lane);
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
@@ -386,7 +385,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
   };
   const int q_end = (a.N + 31) / 32 * 32;
   const int n_steps = (q_end - q_begin) / 32;
-  constexpr int kIssues = 7;   // copy instructions per wave per stage
+  // step 0 has landed once at most one stage's copies of this wave (5 for
+  // waves 0-2, 4 for the others) are outstanding
+  auto wait_first = [&]() __attribute__((always_inline)) {
+    if (wave < 3)
+      wait_vm_le<5>();
+    else
+      wait_vm_le<4>();
+  };
 
   // lane (key j, lg) of an accumulator holds channels 32 cb + 8 i + 4 lg + r
   auto store_rows = [&](float* base, const v16f (&acc)[4]) __attribute__((always_inline)) {
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     };
     issue(0);
     issue(1);
-    wait_vm_le<kIssues>();
+    wait_first();
     barrier_lds();
     if (n_steps > 0) pstep(0);
     for (int t = 0; t + 1 < n_steps; ++t) {
@@ -541,7 +547,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     };
     issue(0);
     issue(1);
-    wait_vm_le<kIssues>();
+    wait_first();
     barrier_lds();
     for (int t = 0; t < n_steps; ++t) {
       wait_vm_le<0>();
