@@ -113,6 +113,31 @@ def unquantised_rows(cfg, plan, q, k, v, rows, sm):
 U_BF16 = 2.0 ** -8
 
 
+def sampled_bounds(qh, kh, vh, o, do, lse, sm, rows, cols, causal):
+    """First-order bounds of the library's bf16 roundings for dQ[rows],
+    dK[cols] and dV[cols]: sm u (P A + |dS|) |K^| for dQ rows, its transpose
+    with |Q^| for dK, 2 u P^T |dO| for dV (A = |dO| |V^|^T), from float64
+    operands [N, d], the forward output o, dO and lse (log2 units)."""
+    l64 = np.asarray(lse, np.float64)
+    o, do = np.asarray(o, np.float64), np.asarray(do, np.float64)
+    dd = (do * o).sum(axis=1)
+    allq = np.arange(qh.shape[0])
+
+    def pmat(ri, ci):
+        s = (qh[ri] @ kh[ci].T) * (sm * OA.LOG2E)
+        p = np.exp2(s - l64[ri][:, None])
+        return np.where(ci[None, :] <= ri[:, None], p, 0.0) if causal else p
+
+    p = pmat(rows, allq)
+    w = p * (np.abs(do[rows]) @ np.abs(vh).T) + np.abs(p * (do[rows] @ vh.T - dd[rows][:, None]))
+    bq = sm * U_BF16 * (w @ np.abs(kh))
+    p = pmat(allq, cols)
+    w = p * (np.abs(do) @ np.abs(vh[cols]).T) + np.abs(p * (do @ vh[cols].T - dd[:, None]))
+    bk = sm * U_BF16 * (w.T @ np.abs(qh))
+    bv = 2 * U_BF16 * (p.T @ np.abs(do))
+    return bq, bk, bv
+
+
 def head_backward_job(job):
     """Backward pass of one head at full size: (config name, shm names of q,
     k, v, dO, shape, head, query rows, keys, bn) -> (head, O [N, d] float32,
@@ -141,22 +166,5 @@ def head_backward_job(job):
     qh, kh, vh = OB.dequantized(qo), OB.dequantized(ko), OB.dequantized(vo)
     do = do.astype(np.float64)
     grads = OB.backward_sampled(qh, kh, vh, o, do, lse, sm, rows, cols, causal=causal)
-    # bounds: sm u (P A + |dS|) |K^| for dQ rows, its transpose with |Q^| for dK,
-    # 2 u P^T |dO| for dV (A = |dO| |V^|^T)
-    l64 = lse.astype(np.float64)
-    dd = (do * o).sum(axis=1)
-    allq = np.arange(n)
-
-    def pmat(ri, ci):
-        s = (qh[ri] @ kh[ci].T) * (sm * OA.LOG2E)
-        p = np.exp2(s - l64[ri][:, None])
-        return np.where(ci[None, :] <= ri[:, None], p, 0.0) if causal else p
-
-    p = pmat(rows, allq)
-    w = p * (np.abs(do[rows]) @ np.abs(vh).T) + np.abs(p * (do[rows] @ vh.T - dd[rows][:, None]))
-    bq = sm * U_BF16 * (w @ np.abs(kh))
-    p = pmat(allq, cols)
-    w = p * (np.abs(do) @ np.abs(vh[cols]).T) + np.abs(p * (do @ vh[cols].T - dd[:, None]))
-    bk = sm * U_BF16 * (w.T @ np.abs(qh))
-    bv = 2 * U_BF16 * (p.T @ np.abs(do))
-    return head, o, lse, grads, (bq, bk, bv)
+    bounds = sampled_bounds(qh, kh, vh, o, do, lse, sm, rows, cols, causal)
+    return head, o, lse, grads, bounds

@@ -104,3 +104,76 @@ def test_maximum_tokens_per_head(gpu_lib, inputs, recipe, causal):
     out = gpu_lib.attention_dense(qq, kq, vq, causal=causal)
     torch.cuda.synchronize()
     _check_output(out, x, causal, "%s %s" % (recipe, "causal" if causal else "dense"))
+
+
+NB = 1 << 20     # the largest tokens per head of pab_attention_backward
+SAMPLES = 64
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_maximum_tokens_per_head(gpu_lib, causal):
+    """The backward at N = 2^20 (its limit), FP8 recipe.  The same
+    construction (equal keys, exactly quantised V) gives the forward in closed
+    form: row i sees n_i keys (N, or i + 1 causal) with one score s_i, so
+    O_i = mean of V over them and LSE_i = s_i + log2(n_i).  Both sides take
+    these O and LSE; the oracle's gradients of sampled rows and keys
+    (backward_sampled) are the reference, under the gate of the other backward
+    tests: each element within twice the first-order bound of the library's
+    bf16 roundings.  dQ is zero in exact arithmetic here (equal keys make the
+    softmax flat in Q), so its mean-abs error is held to the bound alone."""
+    from oracle import attention as OA
+    from oracle import backward as OB
+    from tests.fullsize import sampled_bounds
+    print("max-size backward", "causal" if causal else "dense", flush=True)
+    n, d = NB, D
+    rng = np.random.default_rng(2020 + int(causal))
+    q = torch.from_numpy(rng.standard_normal((n, d)).astype(np.float32)).to(torch.bfloat16)
+    k_row = torch.from_numpy(rng.standard_normal(d).astype(np.float32)).to(torch.bfloat16)
+    idx = rng.integers(0, len(V_TABLE), (n, d), dtype=np.int8)
+    idx[0] = len(V_TABLE) - 1
+    do = torch.from_numpy(rng.standard_normal((n, d)).astype(np.float32)).to(torch.bfloat16)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, SAMPLES, replace=False)]))
+    cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, SAMPLES, replace=False)]))
+
+    # oracle operands and the closed-form forward
+    qc, qs = OQ.fp8_block_quantize(q.float().numpy(), 128)
+    kc, ks = OQ.fp8_block_quantize(np.tile(k_row.float().numpy(), (128, 1)), 128)
+    qh = OB.dequantized(OA.Operand("fp8_block", qc, qs, 128))
+    kh = np.tile(OB.dequantized(OA.Operand("fp8_block", kc, ks, 128))[0], (n, 1))
+    vh = V_TABLE[idx]
+    sm = 1.0 / np.sqrt(d)
+    cnt = np.arange(1, n + 1, dtype=np.float64) if causal else np.full(n, float(n))
+    o = np.ascontiguousarray(np.cumsum(vh, axis=0) / cnt[:, None] if causal else
+                             np.broadcast_to(vh.mean(axis=0), (n, d)), dtype=np.float32)
+    lse = ((qh @ kh[0]) * (sm * OA.LOG2E) + np.log2(cnt)).astype(np.float32)
+
+    dev = torch.device("cuda:0")
+    qq = gpu_lib.quantize(q.view(1, 1, n, d).to(dev), "fp8_block", 128)
+    kq = gpu_lib.quantize(k_row.to(dev).view(1, 1, 1, d).expand(1, 1, n, d), "fp8_block", 128)
+    table = torch.tensor(V_TABLE, dtype=torch.bfloat16, device=dev)
+    vq = gpu_lib.quantize(table[torch.from_numpy(idx).to(dev).long()].view(1, 1, n, d), "fp8_channel")
+    blocks = np.unique(rows // 128)
+    got_qc = qq.codes[0, 0].cpu().numpy()
+    for b in blocks:
+        assert np.array_equal(got_qc[128 * b:128 * b + 128], qc[128 * b:128 * b + 128])
+    assert np.array_equal(qq.scales[0, 0, :n // 128].cpu().numpy(), qs)
+    dq, dk, dv = gpu_lib.attention_backward(
+        qq, kq, vq, torch.from_numpy(o).view(1, 1, n, d).to(dev), do.view(1, 1, n, d).to(dev),
+        torch.from_numpy(lse).view(1, 1, n).to(dev), causal=causal)
+    torch.cuda.synchronize()
+    print("  gpu backward done", flush=True)
+
+    do64 = do.float().numpy().astype(np.float64)
+    ref = OB.backward_sampled(qh, kh, vh, o, do64, lse, sm, rows, cols, causal=causal)
+    bounds = sampled_bounds(qh, kh, vh, o, do64, lse, sm, rows, cols, causal)
+    got = (dq[0, 0, rows].cpu().numpy(), dk[0, 0, cols].cpu().numpy(), dv[0, 0, cols].cpu().numpy())
+    for nm, g, r, b in zip("qkv", got, ref, bounds):
+        assert np.all(np.isfinite(g)), "d%s: non-finite" % nm
+        err = np.abs(g.astype(np.float64) - r)
+        scale = np.abs(r).max()
+        lim = 2 * b + 1e-6 * scale
+        print("  d%s: max err/bound %.3f, max-abs %.3g of max|ref| %.3g" % (
+            nm, (err / lim).max(), err.max(), scale), flush=True)
+        assert np.all(err <= lim), "d%s" % nm
+        assert err.mean() <= 1e-3 * (scale if nm != "q" else 2 * b.max())
