@@ -199,3 +199,34 @@ def test_backward_deterministic(gpu_lib):
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+def test_backward_batch_and_strided_views(gpu_lib):
+    """B = 2, H = 3 with O, dO and the gradient buffers passed as [B, N, H, d]
+    tensors viewed as [B, H, N, d] (token stride H*d): every (b, h) matches
+    the oracle under the element-wise gate, and the gradients land in the
+    caller's strided layout."""
+    B, H, N, d = 2, 3, 200, 128
+    x, ts, do = _inputs(B, H, N, d, 65)
+    sm = 1 / np.sqrt(d)
+    _, bn = gpu_lib.attention_info("fp8_block", d, 0)
+    ops, o_ref, lse_ref = _oracle_lse(x, "fp8", 64, False, sm, bn)
+    q, k, v = _quantize(gpu_lib, [t.cuda() for t in ts], "fp8", 64)
+    o_bnhd = torch.from_numpy(np.ascontiguousarray(o_ref.transpose(0, 2, 1, 3))).cuda()
+    do_bnhd = do.permute(0, 2, 1, 3).contiguous().to(torch.bfloat16).cuda()
+    grads = tuple(torch.full((B, N, H, d), float("nan"), device="cuda").permute(0, 2, 1, 3)
+                  for _ in range(3))
+    dq, dk, dv = gpu_lib.attention_backward(q, k, v, o_bnhd.permute(0, 2, 1, 3), do_bnhd.permute(0, 2, 1, 3),
+                                            torch.from_numpy(lse_ref).cuda(), grads=grads)
+    torch.cuda.synchronize()
+    assert dq.stride() == (N * H * d, d, H * d, 1)
+    got = [t.cpu().numpy() for t in (dq, dk, dv)]
+    do_h = do_bnhd.permute(0, 2, 1, 3).float().cpu().numpy().astype(np.float64)
+    mask = np.ones((N, N), bool)
+    for b in range(B):
+        for h in range(H):
+            qo, ko, vo = ops[b][h]
+            ref = OB.attention_backward(qo, ko, vo, o_ref[b, h], do_h[b, h], lse_ref[b, h], sm_scale=sm)
+            bounds = _error_bounds(qo, ko, vo, o_ref[b, h].astype(np.float64), do_h[b, h],
+                                   lse_ref[b, h].astype(np.float64), sm, mask)
+            _grads_close([g[b, h] for g in got], ref, bounds, "b%d h%d" % (b, h))
