@@ -102,3 +102,21 @@ def test_empty_inputs(gpu_lib, shape, recipe):
     torch.cuda.synchronize()
     x = torch.randn(1, 1, 256, 128, device="cuda")
     assert torch.all(torch.isfinite(api.attention(x, x, x)))
+
+
+@pytest.mark.parametrize("recipe,causal", [("fp8", False), ("fp8", True), ("mxfp4", False)])
+def test_strided_output_equals_contiguous(gpu_lib, recipe, causal):
+    """O written into a caller's [B, N, H, d] buffer viewed as [B, H, N, d]
+    (token stride H*d) equals the contiguous output bit for bit, and every
+    element of the caller's buffer (filled with NaN first) is written."""
+    from precision_attention_block_amd import api
+    B, H, N, d = 2, 3, 520, 128
+    _, ts = _inputs(B, H, N, d, 91, torch.bfloat16, True)
+    qq, kq, vq = api.quantize_qkv(*(t.cuda() for t in ts), recipe, 128)
+    ref = gpu_lib.attention_dense(qq, kq, vq, causal=causal)
+    buf = torch.full((B, N, H, d), float("nan"), device="cuda")
+    got = gpu_lib.attention_dense(qq, kq, vq, causal=causal, out=buf.permute(0, 2, 1, 3))
+    torch.cuda.synchronize()
+    assert got.stride() == (N * H * d, d, H * d, 1)
+    assert torch.equal(got, ref)
+    assert not torch.isnan(buf).any()
