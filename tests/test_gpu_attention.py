@@ -313,3 +313,21 @@ def test_dense_key_tiles_equal_dense(gpu_lib, case):
     assert torch.equal(got, ref)
     assert torch.all(got[:, :, 256:384] == 0)
     assert torch.equal(got_l, ref_l) and torch.equal(got_lse, ref_lse)
+
+
+@pytest.mark.parametrize("recipe,causal,sm", [("fp8", False, 0.3), ("fp8", True, 0.02), ("mxfp4", False, 0.15)])
+def test_custom_softmax_scale(gpu_lib, recipe, causal, sm):
+    """A softmax scale other than 1/sqrt(d) (the scaling_factor argument of the
+    FastVideo call, §5.2) reaches the kernel and matches the oracle with the
+    same scale."""
+    print("softmax scale", recipe, causal, sm, flush=True)
+    N, d = 520, 128
+    x, ts = _inputs(1, 2, N, d, 95, torch.bfloat16, True)
+    blk = 128 if recipe == "fp8" else None
+    _, bn = gpu_lib.attention_info("mxfp4" if recipe == "mxfp4" else "fp8_block", d, 1 if causal else 0)
+    got = _run_dense(gpu_lib, ts, recipe, blk, causal, sm_scale=sm)
+    ref = _oracle_dense(x, recipe, blk, causal, sm, bn)
+    mx, mean = assert_close(got, ref, "sm_scale %g" % sm)
+    default = _oracle_dense(x, recipe, blk, causal, 1 / np.sqrt(d), bn)
+    assert np.abs(default - ref).max() > 100 * mx     # the scale changes the result
+    print("  max-abs %.3g mean-abs %.3g" % (mx, mean))

@@ -230,3 +230,26 @@ def test_backward_batch_and_strided_views(gpu_lib):
             bounds = _error_bounds(qo, ko, vo, o_ref[b, h].astype(np.float64), do_h[b, h],
                                    lse_ref[b, h].astype(np.float64), sm, mask)
             _grads_close([g[b, h] for g in got], ref, bounds, "b%d h%d" % (b, h))
+
+
+@pytest.mark.parametrize("sm", [0.02, 0.25])
+def test_backward_custom_softmax_scale(gpu_lib, sm):
+    """The backward with a softmax scale other than 1/sqrt(d), against the
+    oracle with the same scale (forward O and LSE from the oracle)."""
+    B, H, N, d = 1, 2, 330, 128
+    x, ts, do = _inputs(B, H, N, d, 66)
+    _, bn = gpu_lib.attention_info("fp8_block", d, 1)
+    ops, o_ref, lse_ref = _oracle_lse(x, "fp8", 64, True, sm, bn)
+    q, k, v = _quantize(gpu_lib, [t.cuda() for t in ts], "fp8", 64)
+    dq, dk, dv = gpu_lib.attention_backward(q, k, v, torch.from_numpy(o_ref).cuda(), do.cuda(),
+                                            torch.from_numpy(lse_ref).cuda(), causal=True, sm_scale=sm)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in (dq, dk, dv)]
+    do_h = do.numpy().astype(np.float64)
+    mask = np.tri(N, dtype=bool)
+    for h in range(H):
+        qo, ko, vo = ops[0][h]
+        ref = OB.attention_backward(qo, ko, vo, o_ref[0, h], do_h[0, h], lse_ref[0, h], sm_scale=sm, causal=True)
+        bounds = _error_bounds(qo, ko, vo, o_ref[0, h].astype(np.float64), do_h[0, h],
+                               lse_ref[0, h].astype(np.float64), sm, mask)
+        _grads_close([g[0, h] for g in got], ref, bounds, "sm %g h%d" % (sm, h))
