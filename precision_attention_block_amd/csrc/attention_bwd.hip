@@ -257,6 +257,12 @@ struct Stage {
   static constexpr int R0 = 0, R1 = 8192, T0 = 16384, T1 = 24576, F0 = 32768, F1 = F0 + 256,
                        F2 = F1 + 256, BYTES = F2 + 256;
 };
+// LDS stage of the dQ kernel: K rows, V rows, K^T and two per-token floats.
+// Two stages (49 KB) let three workgroups share a CU.
+constexpr int kDqStages = 2;
+struct DqStage {
+  static constexpr int R0 = 0, R1 = 8192, T0 = 16384, F0 = 24576, F1 = F0 + 256, BYTES = F1 + 256;
+};
 
 __device__ inline v8s lds_row_operand(const uint8_t* base, int row, int chunk) {
   return *reinterpret_cast<const v8s*>(base + row * 256 + 16 * (chunk ^ swz<16>(row)));
@@ -567,7 +573,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
 template <bool CAUSAL, bool UK>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __align__(16) uint8_t st0[Stage::BYTES], st1[Stage::BYTES];
+  __shared__ __align__(16) uint8_t lds[kDqStages * DqStage::BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
@@ -604,11 +610,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   DmaPlan<4> pt;
   pt.init(lane, 64);   // transposed rows of one step are 64 bytes apart
   auto issue = [&](uint8_t* stg, int k0) __attribute__((always_inline)) {
-    issue_rows(kr, stg + Stage::R0, k0, wave, pr);
-    issue_rows(vr, stg + Stage::R1, k0, wave, pr);
-    issue_trans(ktr, stg + Stage::T0, k0, wave, pt);
-    issue_floats(fkr, stg + Stage::F0, k0, lane);
-    issue_floats(kvr, stg + Stage::F1, k0, lane);
+    issue_rows(kr, stg + DqStage::R0, k0, wave, pr);
+    issue_rows(vr, stg + DqStage::R1, k0, wave, pr);
+    issue_trans(ktr, stg + DqStage::T0, k0, wave, pt);
+    issue_floats(fkr, stg + DqStage::F0, k0, lane);
+    issue_floats(kvr, stg + DqStage::F1, k0, lane);
   };
 
   v16f dqt[4];
@@ -628,9 +634,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R0, lr, 2 * ks + lg), qb[ks], s,
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + DqStage::R0, lr, 2 * ks + lg), qb[ks], s,
                                                   0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R1, lr, 2 * ks + lg), gb[ks],
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + DqStage::R1, lr, 2 * ks + lg), gb[ks],
                                                    dp, 0, 0, 0);
     }
   };
@@ -639,7 +645,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       __attribute__((always_inline)) {
     float cs = 0.0f, sc = 0.0f;
     if (UK) {
-      const float fk = *reinterpret_cast<const float*>(cur + Stage::F0);
+      const float fk = *reinterpret_cast<const float*>(cur + DqStage::F0);
       cs = cq * fk;
       sc = a.sm * fk;
     }
@@ -655,7 +661,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       for (int x2 = 0; x2 < 2; ++x2) {
         const int ii = 2 * h + x2;
         float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (!UK) f4 = *reinterpret_cast<const float4*>(cur + Stage::F0 + 4 * (8 * ii + 4 * lg));
+        if (!UK) f4 = *reinterpret_cast<const float4*>(cur + DqStage::F0 + 4 * (8 * ii + 4 * lg));
         const float fk[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -668,7 +674,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int x2 = 0; x2 < 2; ++x2) {
           const int ii = 2 * h + x2;
-          const float4 kv4 = *reinterpret_cast<const float4*>(cur + Stage::F1 + 4 * (8 * ii + 4 * lg));
+          const float4 kv4 = *reinterpret_cast<const float4*>(cur + DqStage::F1 + 4 * (8 * ii + 4 * lg));
           const float kv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -684,23 +690,29 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
-        dqt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + Stage::T0, 32 * cb + lr, 2 * h + lg),
+        dqt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_t_operand(cur + DqStage::T0, 32 * cb + lr, 2 * h + lg),
                                                           db[h], dqt[cb], 0, 0, 0);
   };
 
-  // two stages: step t+1 is copied while step t is computed.  Steps past the
-  // diagonal (causal) are computed and masked: a branch around the products
-  // makes the compiler move the accumulators on every step.
-  issue(st0, 0);
-  int it = 0;
-  for (int k0 = 0; k0 < k_end; k0 += 32, ++it) {
-    const uint8_t* cur = (it & 1) ? st1 : st0;
-    wait_vm_le<0>();
-    barrier_lds();
-    if (k0 + 32 < k_end) issue((it & 1) ? st0 : st1, k0 + 32);
+  // kDqStages stages: the next kDqStages - 1 steps are copied while step t
+  // is computed.  Steps past the diagonal (causal) are computed and masked: a
+  // branch around the products makes the compiler move the accumulators on
+  // every step.  Copies past the last step read zeros or padding (the buffer
+  // descriptors bound them) and are never used.
+  auto stage = [&](int t) __attribute__((always_inline)) {
+    return lds + (t % kDqStages) * DqStage::BYTES;
+  };
+  constexpr int kIssues = 8;   // copy instructions per wave per stage
+  const int n_steps = k_end / 32;
+  for (int t = 0; t + 1 < kDqStages; ++t) issue(stage(t), 32 * t);
+  for (int t = 0; t < n_steps; ++t) {
+    wait_vm_le<(kDqStages - 2) * kIssues>();   // this wave's copies of step t have landed
+    barrier_lds();   // everyone's have; the stage of step t - 1 is free
+    issue(stage(t + kDqStages - 1), 32 * (t + kDqStages - 1));
+    const uint8_t* cur = stage(t);
     v16f s, dp;
     products(cur, s, dp);
-    finish(k0, cur, s, dp);
+    finish(32 * t, cur, s, dp);
   }
   wait_vm_le<0>();
   if (i < a.N) {
