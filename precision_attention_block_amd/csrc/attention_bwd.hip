@@ -258,8 +258,6 @@ struct Stage {
                        F2 = F1 + 256, BYTES = F2 + 256;
 };
 // LDS stage of the dQ kernel: K rows, V rows, K^T and two per-token floats.
-// Two stages (49 KB) let three workgroups share a CU.
-constexpr int kDqStages = 2;
 struct DqStage {
   static constexpr int R0 = 0, R1 = 8192, T0 = 16384, F0 = 24576, F1 = F0 + 256, BYTES = F1 + 256;
 };
@@ -571,9 +569,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
 // UK: the K block scale is the same for all 32 keys of a step (MXFP4, or FP8
 // blocks of a multiple of 32 tokens).
 template <bool CAUSAL, bool UK>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __align__(16) uint8_t lds[kDqStages * DqStage::BYTES];
+  __shared__ __align__(16) uint8_t lds[3 * DqStage::BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
@@ -694,26 +692,36 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
                                                           db[h], dqt[cb], 0, 0, 0);
   };
 
-  // kDqStages stages: the next kDqStages - 1 steps are copied while step t
-  // is computed.  Steps past the diagonal (causal) are computed and masked: a
-  // branch around the products makes the compiler move the accumulators on
-  // every step.  Copies past the last step read zeros or padding (the buffer
-  // descriptors bound them) and are never used.
-  auto stage = [&](int t) __attribute__((always_inline)) {
-    return lds + (t % kDqStages) * DqStage::BYTES;
-  };
+  // Software pipeline over 32-key steps t (three LDS stages): iteration t
+  // copies step t+2, forms the scores of step t+1 while the vector unit works
+  // on step t, then adds step t's products.  Steps past the diagonal (causal)
+  // are computed and masked: a branch around the products makes the compiler
+  // move the accumulators on every step.  Past the last step the copies (read
+  // as padding or zeros, bounded by the buffer descriptors) and the score
+  // products are never used.
+  auto stage = [&](int t) __attribute__((always_inline)) { return lds + (t % 3) * DqStage::BYTES; };
   constexpr int kIssues = 8;   // copy instructions per wave per stage
   const int n_steps = k_end / 32;
-  for (int t = 0; t + 1 < kDqStages; ++t) issue(stage(t), 32 * t);
-  for (int t = 0; t < n_steps; ++t) {
-    wait_vm_le<(kDqStages - 2) * kIssues>();   // this wave's copies of step t have landed
-    barrier_lds();   // everyone's have; the stage of step t - 1 is free
-    issue(stage(t + kDqStages - 1), 32 * (t + kDqStages - 1));
-    const uint8_t* cur = stage(t);
-    v16f s, dp;
-    products(cur, s, dp);
-    finish(32 * t, cur, s, dp);
+  issue(stage(0), 0);
+  issue(stage(1), 32);
+  wait_vm_le<kIssues>();
+  barrier_lds();
+  v16f sa, dpa, sb, dpb;
+  products(stage(0), sa, dpa);
+  auto body = [&](const int t, v16f& s_cur, v16f& dp_cur, v16f& s_nxt, v16f& dp_nxt)
+      __attribute__((always_inline)) {
+    wait_vm_le<0>();
+    barrier_lds();   // step t+1 has landed everywhere; stage (t+2) % 3 is free
+    issue(stage(t + 2), 32 * (t + 2));
+    products(stage(t + 1), s_nxt, dp_nxt);
+    finish(32 * t, stage(t), s_cur, dp_cur);
+  };
+  int t = 0;
+  for (; t + 2 <= n_steps; t += 2) {
+    body(t, sa, dpa, sb, dpb);
+    body(t + 1, sb, dpb, sa, dpa);
   }
+  if (t < n_steps) finish(32 * t, stage(t), sa, dpa);   // odd count: the last step
   wait_vm_le<0>();
   if (i < a.N) {
     const int b = bh / a.H, h = bh % a.H;
