@@ -426,8 +426,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) dvt[cb][e] = 0.0f;
-    // S, P and dV of step t (stage t % 3); P goes to exchange slot t & 1
-    auto pstep = [&](const int t) __attribute__((always_inline)) {
+    // S and P of step t (stage t % 3): P goes to exchange slot t & 1 and,
+    // packed as bf16 B operands, to pb for dV.  `before` runs between the
+    // score products and the vector work (the previous step's dV products,
+    // which do not depend on these scores).
+    auto pstep = [&](const int t, v8s (&pb)[2], auto&& before) __attribute__((always_inline)) {
       const uint8_t* cur = stage(t);
       const int q0 = q_begin + 32 * t;
       v16f s;
@@ -437,6 +440,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
       for (int ks = 0; ks < 8; ++ks)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand(cur + Stage::R0, lr, 2 * ks + lg), kb[ks],
                                                     s, 0, 0, 0);
+      before();
       float cs = 0.0f;
       if (UQ) cs = ck * *reinterpret_cast<const float*>(cur + Stage::F2);
       const bool masked = !all_valid || (CAUSAL && q0 < key0 + 32);
@@ -465,13 +469,15 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         *reinterpret_cast<float4*>(x + k * 1024) = make_float4(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]);
-      v8s pb[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         pb[h] = __builtin_bit_cast(v8s, make_uint4(bf16x2(p[8 * h], p[8 * h + 1]), bf16x2(p[8 * h + 2], p[8 * h + 3]),
                                                    bf16x2(p[8 * h + 4], p[8 * h + 5]),
                                                    bf16x2(p[8 * h + 6], p[8 * h + 7])));
-      // dV^T += dO^T P (channels x keys, K = queries)
+    };
+    // dV^T += dO^T P of step t (channels x keys, K = queries)
+    auto dvstep = [&](const int t, const v8s (&pb)[2]) __attribute__((always_inline)) {
+      const uint8_t* cur = stage(t);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -479,20 +485,40 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
           dvt[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               lds_t_operand(cur + Stage::T1, 32 * cb + lr, 2 * h + lg), pb[h], dvt[cb], 0, 0, 0);
     };
+    // dV runs one step behind: iteration t forms the scores of step t+1, adds
+    // step t's dV products while they complete, then forms P of step t+1.
+    // Stage t stays valid through iteration t (the copy of that iteration
+    // goes to stage t+2).
     issue(0);
     issue(1);
     wait_first();
     barrier_lds();
-    if (n_steps > 0) pstep(0);
-    for (int t = 0; t + 1 < n_steps; ++t) {
+    v8s pba[2], pbb[2];
+    pstep(0, pba, [] {});
+    auto body = [&](const int t, const v8s (&pb_cur)[2], v8s (&pb_nxt)[2]) __attribute__((always_inline)) {
       wait_vm_le<0>();
       barrier_lds();   // step t+1 has landed; stage (t+2) % 3 and slot (t+1) & 1 are free
       issue(t + 2);
-      pstep(t + 1);
+      pstep(t + 1, pb_nxt, [&] { dvstep(t, pb_cur); });
+    };
+    int t = 0;
+    for (; t + 3 <= n_steps; t += 2) {
+      body(t, pba, pbb);
+      body(t + 1, pbb, pba);
     }
-    wait_vm_le<0>();
-    barrier_lds();     // the dS-waves' last step
-    issue(n_steps + 1);
+    if (t + 2 <= n_steps) {   // one more step to form: P of step t+1 goes to pbb
+      body(t, pba, pbb);
+      ++t;
+      wait_vm_le<0>();
+      barrier_lds();   // the dS-waves' last step
+      issue(n_steps + 1);
+      dvstep(t, pbb);
+    } else {
+      wait_vm_le<0>();
+      barrier_lds();   // the dS-waves' last step
+      issue(n_steps + 1);
+      dvstep(t, pba);
+    }
     wait_vm_le<0>();   // no copy may still target this workgroup's LDS when it ends
     store_rows(a.dv, dvt);
   } else {
