@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void bwd_prep_do_kernel(BwdArgs a) {
   float acc = 0.0f;
 #pragma unroll
   for (int c8 = 0; c8 < 4; ++c8) {
-    const int c0 = 32 * part + 8 * c8;
+    const int c0 = 8 * part + 32 * c8;   // the 4 threads of a token read 128 contiguous bytes
     float gv[8], ov[8];
     if (live) {
       load8(g + c0, gv);
