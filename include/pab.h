@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PAB_ABI_VERSION 6
+#define PAB_ABI_VERSION 7
 #define PAB_TOKEN_ALIGN 128  /* query tile of the attention kernel */
 #define PAB_MAX_TAU 8        /* largest softmax rescale threshold (log2 units) */
 
@@ -318,6 +318,28 @@ pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const 
                                   const int64_t dout_strides[4], const float* lse, float* dq,
                                   float* dk, float* dv, const int64_t grad_strides[4],
                                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Backward of sliding-tile attention (pab_attention_sta): the gradients of
+ * pab_attention_backward, with key j visible to query i when the tile of j is
+ * in the window list of the tile of i and kv_valid[j] is nonzero [FPS] §2.2.
+ * The tokens are in the kernel's tile-major order (the forward called without
+ * out_perm, which gives out and lse in that order).  The window relation must
+ * be symmetric (v in W(u) exactly when u in W(v)), as the windows of
+ * pab_sta_plan are: the key tiles of query tile u are read from W(u) and the
+ * query tiles that see key tile v from W(v); a tile with an empty list gets
+ * zero gradients.  win_off int32 [n_tiles + 1],
+ * win_idx int32 [win_off[n_tiles]] on the device; n_tiles * tile_tokens = N,
+ * tile_tokens a multiple of PAB_TOKEN_ALIGN.  Every other argument, the
+ * workspace and the errors are as for pab_attention_backward. */
+pab_status pab_attention_sta_backward(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                      float sm_scale, const int32_t* win_off,
+                                      const int32_t* win_idx, int n_tiles, int tile_tokens,
+                                      const uint8_t* kv_valid, const float* out,
+                                      const int64_t out_strides[4], const void* dout,
+                                      pab_dtype dout_dtype, const int64_t dout_strides[4],
+                                      const float* lse, float* dq, float* dk, float* dv,
+                                      const int64_t grad_strides[4], void* workspace,
+                                      int64_t workspace_bytes, void* stream);
 
 /*
  * pab_sta_plan - host-side planner for sliding-tile attention [FPS §2.2,

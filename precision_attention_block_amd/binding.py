@@ -22,7 +22,7 @@ EXPORTS = [
     "pab_abi_version", "pab_status_str", "pab_last_hip_error", "pab_token_alloc",
     "pab_attention_info", "pab_quantize", "pab_attention_dense", "pab_attention_sta",
     "pab_sta_plan", "pab_count_nonfinite", "pab_attention_backward_workspace",
-    "pab_attention_backward", "pab_attention_dense_tiles", "pab_key_tiles",
+    "pab_attention_backward", "pab_attention_sta_backward", "pab_attention_dense_tiles", "pab_key_tiles",
     "pab_attention_sta_steps", "pab_sta_steps",
 ]
 
@@ -91,6 +91,10 @@ def _lib():
         L.pab_attention_backward.argtypes = [ctypes.POINTER(QView)] * 3 + [
             ctypes.c_int, ctypes.c_float, vp, vp, i64p, vp, ctypes.c_int, i64p, vp, vp, vp, vp,
             i64p, vp, ctypes.c_int64, vp]
+        L.pab_attention_sta_backward.restype = ctypes.c_int
+        L.pab_attention_sta_backward.argtypes = [ctypes.POINTER(QView)] * 3 + [
+            ctypes.c_float, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp, i64p, vp, ctypes.c_int, i64p,
+            vp, vp, vp, vp, i64p, vp, ctypes.c_int64, vp]
         ip = ctypes.POINTER(ctypes.c_int)
         L.pab_sta_plan.restype = ctypes.c_int
         L.pab_sta_plan.argtypes = [ip, ip, ip, ip, vp, vp, vp, vp, vp, vp, i64p, i64p, i64p]
@@ -312,6 +316,37 @@ def attention_backward(q, k, v, out, dout, lse, causal=False, sm_scale=None, kv_
         ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()), _i64(dq.stride()),
         ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(dev))
     _check(st, "pab_attention_backward")
+    return dq, dk, dv
+
+
+def attention_sta_backward(q, k, v, plan, out, dout, lse, sm_scale=None, use_kv_valid=True,
+                           workspace=None, grads=None):
+    """Gradients (dQ, dK, dV) of attention_sta (a DevicePlan), float32
+    [B, H, N, d] in the kernel's tile-major token order; out and lse come from
+    attention_sta called with use_out_perm=False (pab_attention_sta_backward)."""
+    import torch
+    dev = out.device
+    if workspace is None:
+        workspace = torch.empty(backward_workspace_bytes(q.B, q.H, q.N, q.d), dtype=torch.uint8,
+                                device=dev)
+    if grads is None:
+        grads = tuple(torch.empty((q.B, q.H, q.N, q.d), dtype=torch.float32, device=dev)
+                      for _ in range(3))
+    dq, dk, dv = grads
+    if dk.stride() != dq.stride() or dv.stride() != dq.stride():
+        raise ValueError("dq, dk and dv must share strides")
+    dt = {torch.float32: PAB_F32, torch.bfloat16: PAB_BF16}[dout.dtype]
+    qv, kv, vv = q.view(), k.view(), v.view()
+    st = _lib().pab_attention_sta_backward(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(sm_scale or 0.0),
+        ctypes.c_void_p(plan.win_off.data_ptr()), ctypes.c_void_p(plan.win_idx.data_ptr()),
+        int(plan.n_tiles), int(plan.tile_tokens),
+        ctypes.c_void_p(plan.kv_valid.data_ptr() if use_kv_valid else 0),
+        ctypes.c_void_p(out.data_ptr()), _i64(out.stride()), ctypes.c_void_p(dout.data_ptr()), dt,
+        _i64(dout.stride()), ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(dq.data_ptr()),
+        ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()), _i64(dq.stride()),
+        ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(dev))
+    _check(st, "pab_attention_sta_backward")
     return dq, dk, dv
 
 

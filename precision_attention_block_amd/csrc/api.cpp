@@ -397,13 +397,16 @@ int64_t pab_attention_backward_workspace(int64_t B, int64_t H, int64_t N, int64_
   return pab::bwd_workspace_layout(B * H, round_up(N, PAB_TOKEN_ALIGN), d, off);
 }
 
-pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const pab_qview* v,
-                                  int causal, float sm_scale, const uint8_t* kv_valid,
-                                  const float* out, const int64_t out_strides[4],
-                                  const void* dout, pab_dtype dout_dtype,
-                                  const int64_t dout_strides[4], const float* lse, float* dq,
-                                  float* dk, float* dv, const int64_t grad_strides[4],
-                                  void* workspace, int64_t workspace_bytes, void* stream) {
+// The backward of dense / causal attention (win_idx NULL) or of sliding-tile
+// attention over the CSR window lists (validated by the caller).
+static pab_status backward_impl(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                int causal, float sm_scale, const uint8_t* kv_valid,
+                                const int32_t* win_off, const int32_t* win_idx, int tile_tokens,
+                                const float* out, const int64_t out_strides[4],
+                                const void* dout, pab_dtype dout_dtype,
+                                const int64_t dout_strides[4], const float* lse, float* dq,
+                                float* dk, float* dv, const int64_t grad_strides[4],
+                                void* workspace, int64_t workspace_bytes, void* stream) {
   if (empty_views(q, k, v)) return PAB_OK;
   pab_status s;
   if ((s = check_view(q, 0)) != PAB_OK) return s;
@@ -474,6 +477,9 @@ pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const 
   else
     a.v_scale = static_cast<const float*>(v->scales);
   a.kv_valid = kv_valid;
+  a.win_off = win_off;
+  a.win_idx = win_idx;
+  a.tile_tokens = tile_tokens;
   a.o = out;
   a.o_sb = out_strides[0];
   a.o_sh = out_strides[1];
@@ -502,6 +508,38 @@ pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const 
   a.kvf = ws32(11);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(pab::launch_attention_backward(a, st), st);
+}
+
+pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                  int causal, float sm_scale, const uint8_t* kv_valid,
+                                  const float* out, const int64_t out_strides[4],
+                                  const void* dout, pab_dtype dout_dtype,
+                                  const int64_t dout_strides[4], const float* lse, float* dq,
+                                  float* dk, float* dv, const int64_t grad_strides[4],
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, causal, sm_scale, kv_valid, nullptr, nullptr, 0, out, out_strides,
+                       dout, dout_dtype, dout_strides, lse, dq, dk, dv, grad_strides, workspace,
+                       workspace_bytes, stream);
+}
+
+pab_status pab_attention_sta_backward(const pab_qview* q, const pab_qview* k, const pab_qview* v,
+                                      float sm_scale, const int32_t* win_off,
+                                      const int32_t* win_idx, int n_tiles, int tile_tokens,
+                                      const uint8_t* kv_valid, const float* out,
+                                      const int64_t out_strides[4], const void* dout,
+                                      pab_dtype dout_dtype, const int64_t dout_strides[4],
+                                      const float* lse, float* dq, float* dk, float* dv,
+                                      const int64_t grad_strides[4], void* workspace,
+                                      int64_t workspace_bytes, void* stream) {
+  if (empty_views(q, k, v)) return PAB_OK;
+  if (!q || !win_off || !win_idx || !aligned(win_off, 4) || !aligned(win_idx, 4))
+    return PAB_INVALID_ARG;
+  if (n_tiles < 1 || tile_tokens < PAB_TOKEN_ALIGN || tile_tokens % PAB_TOKEN_ALIGN)
+    return PAB_INVALID_ARG;
+  if ((int64_t)n_tiles * tile_tokens != q->N) return PAB_INVALID_ARG;
+  return backward_impl(q, k, v, 0, sm_scale, kv_valid, win_off, win_idx, tile_tokens, out,
+                       out_strides, dout, dout_dtype, dout_strides, lse, dq, dk, dv, grad_strides,
+                       workspace, workspace_bytes, stream);
 }
 
 pab_status pab_sta_plan(const int grid[3], const int real_grid[3], const int tile[3],

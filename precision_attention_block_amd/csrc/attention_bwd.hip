@@ -349,7 +349,9 @@ __device__ inline void issue_stage8(uint8_t* stg, int q0, int wave, int lane,
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <bool CAUSAL, bool UQ>
+// STA: the queries are the tiles of the key tile's window list, each walked
+// in 32-query steps (no causal mask).
+template <bool CAUSAL, bool UQ, bool STA>
 __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __align__(16) uint8_t lds[PairLds::BYTES];
@@ -384,11 +386,33 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     return lds + PairLds::PX + (t & 1) * PairLds::PX_BYTES + kblk * 4096 + 16 * lane;
   };
   const int q_begin = CAUSAL ? kt * kBwdTile : 0;   // earlier queries see none of these keys
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    issue_stage8(stage(t), q_begin + 32 * t, wave, lane, qr, dr, qtr, dtr, lsr, ddr, fqr, pr, pt);
-  };
   const int q_end = (a.N + 31) / 32 * 32;
-  const int n_steps = (q_end - q_begin) / 32;
+  const int spt = STA ? a.tile_tokens / 32 : 1;     // steps per tile
+  const int32_t* wl = nullptr;
+  int n_steps = (q_end - q_begin) / 32;
+  if (STA) {
+    const int v = kt * kBwdTile / a.tile_tokens;
+    wl = a.win_idx + a.win_off[v];
+    n_steps = (a.win_off[v + 1] - a.win_off[v]) * spt;
+    if (n_steps <= 0) {   // an empty window list: no query sees these keys
+      if (j < a.N) {
+        const int b = bh / a.H, h = bh % a.H;
+        float* row = (pwave ? a.dv : a.dk) + b * a.g_sb + h * a.g_sh + (int64_t)j * a.g_sn;
+        for (int c = 4 * lg; c < kD; c += 8)
+          *reinterpret_cast<float4*>(row + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      return;
+    }
+  }
+  // first query of step t; the copies issued past the last step repeat it
+  auto qstart = [&](int t) __attribute__((always_inline)) -> int {
+    if (!STA) return q_begin + 32 * t;
+    const int tc = t < n_steps ? t : n_steps - 1;
+    return a.tile_tokens * __builtin_amdgcn_readfirstlane(wl[tc / spt]) + 32 * (tc % spt);
+  };
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    issue_stage8(stage(t), qstart(t), wave, lane, qr, dr, qtr, dtr, lsr, ddr, fqr, pr, pt);
+  };
   // step 0 has landed once at most one stage's copies of this wave (5 for
   // waves 0-2, 4 for the others) are outstanding
   auto wait_first = [&]() __attribute__((always_inline)) {
@@ -432,7 +456,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
     // which do not depend on these scores).
     auto pstep = [&](const int t, v8s (&pb)[2], auto&& before) __attribute__((always_inline)) {
       const uint8_t* cur = stage(t);
-      const int q0 = q_begin + 32 * t;
+      const int q0 = qstart(t);
       v16f s;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] = 0.0f;
@@ -594,7 +618,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(BwdArgs a) {
 // ---- dQ -------------------------------------------------------------------------
 // UK: the K block scale is the same for all 32 keys of a step (MXFP4, or FP8
 // blocks of a multiple of 32 tokens).
-template <bool CAUSAL, bool UK>
+// STA: the keys are the tiles of the query tile's window list.
+template <bool CAUSAL, bool UK, bool STA>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __align__(16) uint8_t lds[3 * DqStage::BYTES];
@@ -727,9 +752,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   // products are never used.
   auto stage = [&](int t) __attribute__((always_inline)) { return lds + (t % 3) * DqStage::BYTES; };
   constexpr int kIssues = 8;   // copy instructions per wave per stage
-  const int n_steps = k_end / 32;
-  issue(stage(0), 0);
-  issue(stage(1), 32);
+  const int spt = STA ? a.tile_tokens / 32 : 1;     // steps per tile
+  const int32_t* wl = nullptr;
+  int n_steps = k_end / 32;
+  if (STA) {
+    const int u = qt * kBwdTile / a.tile_tokens;
+    wl = a.win_idx + a.win_off[u];
+    n_steps = (a.win_off[u + 1] - a.win_off[u]) * spt;
+    if (n_steps <= 0) {   // an empty window list: this query sees no key
+      if (i < a.N) {
+        const int b = bh / a.H, h = bh % a.H;
+        float* row = a.dq + b * a.g_sb + h * a.g_sh + (int64_t)i * a.g_sn;
+        for (int c = 4 * lg; c < kD; c += 8)
+          *reinterpret_cast<float4*>(row + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      return;
+    }
+  }
+  // first key of step t; the copies issued past the last step repeat it
+  auto kstart = [&](int t) __attribute__((always_inline)) -> int {
+    if (!STA) return 32 * t;
+    const int tc = t < n_steps ? t : n_steps - 1;
+    return a.tile_tokens * __builtin_amdgcn_readfirstlane(wl[tc / spt]) + 32 * (tc % spt);
+  };
+  issue(stage(0), kstart(0));
+  issue(stage(1), kstart(1));
   wait_vm_le<kIssues>();
   barrier_lds();
   v16f sa, dpa, sb, dpb;
@@ -738,16 +785,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       __attribute__((always_inline)) {
     wait_vm_le<0>();
     barrier_lds();   // step t+1 has landed everywhere; stage (t+2) % 3 is free
-    issue(stage(t + 2), 32 * (t + 2));
+    issue(stage(t + 2), kstart(t + 2));
     products(stage(t + 1), s_nxt, dp_nxt);
-    finish(32 * t, stage(t), s_cur, dp_cur);
+    finish(kstart(t), stage(t), s_cur, dp_cur);
   };
   int t = 0;
   for (; t + 2 <= n_steps; t += 2) {
     body(t, sa, dpa, sb, dpb);
     body(t + 1, sb, dpb, sa, dpa);
   }
-  if (t < n_steps) finish(32 * t, stage(t), sa, dpa);   // odd count: the last step
+  if (t < n_steps) finish(kstart(t), stage(t), sa, dpa);   // odd count: the last step
   wait_vm_le<0>();
   if (i < a.N) {
     const int b = bh / a.H, h = bh % a.H;
@@ -781,24 +828,33 @@ hipError_t launch_attention_backward(const BwdArgs& a, hipStream_t st) {
   // the Q scale is uniform over 32-query steps for MXFP4 (1) and for FP8 blocks of 32k tokens
   const bool uq = a.qk_mx || a.blk_q % 32 == 0;
   const bool uk = a.qk_mx || a.blk_k % 32 == 0;
-  if (a.causal) {
+  if (a.win_idx) {
     if (uq)
-      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<true, true>), gt, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<false, true, true>), gt, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<true, false>), gt, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<false, false, true>), gt, dim3(512), 0, st, a);
     if (uk)
-      hipLaunchKernelGGL((bwd_dq_kernel<true, true>), gt, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<false, true, true>), gt, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<true, false>), gt, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<false, false, true>), gt, dim3(256), 0, st, a);
+  } else if (a.causal) {
+    if (uq)
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<true, true, false>), gt, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<true, false, false>), gt, dim3(512), 0, st, a);
+    if (uk)
+      hipLaunchKernelGGL((bwd_dq_kernel<true, true, false>), gt, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<true, false, false>), gt, dim3(256), 0, st, a);
   } else {
     if (uq)
-      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<false, true>), gt, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<false, true, false>), gt, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<false, false>), gt, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<false, false, false>), gt, dim3(512), 0, st, a);
     if (uk)
-      hipLaunchKernelGGL((bwd_dq_kernel<false, true>), gt, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<false, true, false>), gt, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<false, false>), gt, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<false, false, false>), gt, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

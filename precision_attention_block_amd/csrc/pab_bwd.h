@@ -33,6 +33,13 @@ struct BwdArgs {
   const float* v_scale;        // FP8: [BH][d]
   const uint8_t* v_e8;         // MXFP4: [BH][n_alloc/32][d] (channels interleaved)
   const uint8_t* kv_valid;     // nullable [N]
+  // sliding-tile attention (nullable): CSR window lists of the tiles of
+  // tile_tokens tokens (kernel token order).  The window relation is
+  // symmetric, so W(v) lists both the key tiles of query tile v and the
+  // query tiles that see key tile v.
+  const int32_t* win_off;
+  const int32_t* win_idx;
+  int tile_tokens;
   // forward outputs and the upstream gradient
   const float* o;              // [B,H,N,d], strides o_s*
   int64_t o_sb, o_sh, o_sn;

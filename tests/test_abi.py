@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(B):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(B.lib(), name), name
-    assert B.lib().pab_abi_version() == 6
+    assert B.lib().pab_abi_version() == 7
 
 
 def test_token_alloc_and_info(B):
@@ -294,4 +294,28 @@ def test_size_limits_without_device(B):
     assert L.pab_attention_backward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, 0.0, null,
                                     fake, st, fake, 0, st, fake, fake, fake, fake, st,
                                     ctypes.c_void_p(4096 * 256), 1 << 40, null) == B.PAB_UNSUPPORTED
+    assert L.pab_last_hip_error() == 0
+
+
+def test_sta_backward_validation_without_device(B):
+    """pab_attention_sta_backward rejects bad window arguments before any
+    launch; the rest of its validation is pab_attention_backward's."""
+    L = B.lib()
+    fake = 4096
+    mk = lambda recipe: B.QView(fake, fake, fake, recipe, 128, 1, 2, 256, 128)
+    qv, kv, vv = mk(0), mk(0), mk(1)
+    st = B._i64([2 * 256 * 128, 256 * 128, 128, 1])
+    null = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(fake)
+    need = L.pab_attention_backward_workspace(1, 2, 256, 128)
+
+    def sta(win_off=f, win_idx=f, n_tiles=2, tile=128, nbytes=need):
+        return L.pab_attention_sta_backward(
+            ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), 0.0, win_off, win_idx, n_tiles, tile,
+            null, f, st, f, B.PAB_F32, st, f, f, f, f, st, ctypes.c_void_p(fake * 16), nbytes, null)
+    assert sta(win_off=null) == B.PAB_INVALID_ARG
+    assert sta(win_idx=ctypes.c_void_p(fake + 2)) == B.PAB_INVALID_ARG      # misaligned list
+    assert sta(tile=100) == B.PAB_INVALID_ARG                               # not a multiple of 128
+    assert sta(n_tiles=3) == B.PAB_INVALID_ARG                              # tiles do not cover N
+    assert sta(nbytes=need - 1) == B.PAB_INVALID_ARG                        # workspace too small
     assert L.pab_last_hip_error() == 0

@@ -253,3 +253,51 @@ def test_backward_custom_softmax_scale(gpu_lib, sm):
         bounds = _error_bounds(qo, ko, vo, o_ref[0, h].astype(np.float64), do_h[0, h],
                                lse_ref[0, h].astype(np.float64), sm, mask)
         _grads_close([g[0, h] for g in got], ref, bounds, "sm %g h%d" % (sm, h))
+
+
+def test_sta_backward_parity(gpu_lib):
+    """Backward of sliding-tile attention (pab_attention_sta_backward) on a
+    padded grid: 16 tiles of 128 tokens, window (1, 3, 3), so a tile sees at
+    most 9 of them.  Both sides take the oracle's per-tile forward (kernel
+    token order); the reference is the oracle backward with the token-level
+    mask "tile of j in the window of the tile of i, and key j valid", under
+    the element-wise gate."""
+    from oracle import sta as OS
+    grid, real, tile, window = (2, 32, 32), (2, 30, 29), (2, 8, 8), (1, 3, 3)
+    hp = gpu_lib.sta_plan(grid, real, tile, window)
+    dp = gpu_lib.DevicePlan(hp)
+    op = OS.plan(grid, real, tile, window)
+    B, H, N, d, tt = 1, 2, hp.n_tokens, 128, hp.tile_tokens
+    x, ts, do = _inputs(B, H, N, d, 67)
+    sm = 1 / np.sqrt(d)
+    _, bn = gpu_lib.attention_info("fp8_block", d, 2)
+    ops = oracle_operands(*x, "fp8", tt)
+    o_ref = np.zeros((B, H, N, d), np.float32)
+    lse_ref = np.zeros((B, H, N), np.float32)
+    for h in range(H):
+        qo, ko, vo = ops[0][h]
+        for u in range(op.n_tiles):
+            rows = np.arange(u * tt, (u + 1) * tt)
+            o_ref[0, h, rows], lse_ref[0, h, rows] = OA.recipe_attention(
+                qo, ko, vo, rows, sm_scale=sm, bn=bn, kv_valid=op.kv_valid,
+                key_blocks=OS.key_blocks_for_tile(op, u, bn), return_lse=True)
+    tiles_of = np.arange(N) // tt
+    see = np.zeros((op.n_tiles, op.n_tiles), bool)
+    for u in range(op.n_tiles):
+        see[u, op.win_idx[op.win_off[u]:op.win_off[u + 1]]] = True
+    assert np.array_equal(see, see.T) and not see.all()
+    mask = see[tiles_of][:, tiles_of] & op.kv_valid.astype(bool)[None, :]
+    q, k, v = _quantize(gpu_lib, [t.cuda() for t in ts], "fp8", tt)
+    print("sta backward: %d tiles, %d pairs, N = %d" % (op.n_tiles, int(see.sum()), N), flush=True)
+    dq, dk, dv = gpu_lib.attention_sta_backward(q, k, v, dp, torch.from_numpy(o_ref).cuda(), do.cuda(),
+                                                torch.from_numpy(lse_ref).cuda())
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in (dq, dk, dv)]
+    do_h = do.numpy().astype(np.float64)
+    for h in range(H):
+        qo, ko, vo = ops[0][h]
+        qh, kh, vh = OB.dequantized(qo), OB.dequantized(ko), OB.dequantized(vo)
+        ref = OB.backward_core(qh, kh, vh, o_ref[0, h], do_h[0, h], lse_ref[0, h], sm, mask)
+        bounds = _error_bounds(qo, ko, vo, o_ref[0, h].astype(np.float64), do_h[0, h],
+                               lse_ref[0, h].astype(np.float64), sm, mask)
+        _grads_close([g[0, h] for g in got], ref, bounds, "sta h%d" % h)
