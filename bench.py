@@ -181,21 +181,30 @@ def time_gpu(path, steps, warmup):
 
 
 def time_backward(cfg, path, steps, warmup):
-    """The backward pass (prep kernels, dK/dV, dQ) of the dense or causal
-    workload: one forward with the row statistic, then `steps` timed backward
-    calls on a seeded bf16 dO; returns per-call milliseconds."""
+    """The backward pass (prep kernels, dK/dV, dQ) of the dense, causal or
+    sliding-tile workload: one forward with the row statistic (sliding-tile:
+    in the kernel's token order), then `steps` timed backward calls on a seeded
+    bf16 dO; returns per-call milliseconds."""
     import torch
     lib = path.lib
     qq, kq, vq = path.quantize()
     causal = cfg.mode == "causal"
-    out, lse = lib.attention_dense(qq, kq, vq, causal=causal, lse=True)
+    sta = cfg.mode == "sta"
+    if sta:
+        out, lse = lib.attention_sta(qq, kq, vq, path.dplan, use_out_perm=False, lse=True, steps=True)
+    else:
+        out, lse = lib.attention_dense(qq, kq, vq, causal=causal, lse=True)
     g = torch.Generator(device="cpu").manual_seed(1000 * cfg.index + 7)
     dout = torch.randn(out.shape, generator=g).to(torch.bfloat16).cuda()
     ws = torch.empty(lib.backward_workspace_bytes(cfg.B, cfg.H, cfg.n_kernel, cfg.d),
                      dtype=torch.uint8, device="cuda")
     grads = tuple(torch.empty_like(out) for _ in range(3))
-    call = lambda: lib.attention_backward(qq, kq, vq, out, dout, lse, causal=causal,
-                                          workspace=ws, grads=grads)
+    if sta:
+        call = lambda: lib.attention_sta_backward(qq, kq, vq, path.dplan, out, dout, lse,
+                                                  workspace=ws, grads=grads)
+    else:
+        call = lambda: lib.attention_backward(qq, kq, vq, out, dout, lse, causal=causal,
+                                              workspace=ws, grads=grads)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -213,14 +222,16 @@ def time_backward(cfg, path, steps, warmup):
 
 
 def backward_main(args, cfg, path):
-    if cfg.mode not in ("dense", "causal") or path.dplan is not None:
-        print("--backward runs the dense and causal workloads (the backward pass has no "
-              "sliding-tile or token-permuted form)", file=sys.stderr)
+    if cfg.mode not in ("dense", "causal", "sta") or (cfg.mode != "sta" and path.dplan is not None):
+        print("--backward runs the dense, causal and sliding-tile workloads (the backward pass "
+              "has no token-permuted dense form)", file=sys.stderr)
         sys.exit(2)
     print("[bench] timing %d backward steps after %d warm-up" % (args.steps, args.warmup),
           file=sys.stderr, flush=True)
     wall, ms = time_backward(cfg, path, args.steps, args.warmup)
-    flops = 2.5 * algorithmic_flops(cfg, None)       # five products of 2 N^2 d (causal: half)
+    # five products of 2 d per computed (query, key) pair (causal: half; sliding-tile: the
+    # real pairs of the windows)
+    flops = 2.5 * algorithmic_flops(cfg, path.plan if cfg.mode == "sta" else None)
     ms_call = float(np.mean(ms))
     achieved = flops / (ms_call * 1e-3) / 1e12
     result = {

@@ -265,9 +265,9 @@ def attention_sta(q, k, v, plan, sm_scale=None, use_kv_valid=True, use_out_perm=
     lse as in attention_dense.  steps: walk the plan's BN-key step lists,
     which leave out the steps without a valid key (pab_attention_sta_steps;
     same result, less work on a padded grid)."""
-    n_out = plan.n_real if n_out is None else int(n_out)
-    if not use_out_perm and n_out is None:
-        n_out = q.N
+    if n_out is None:   # caller order: the real tokens; kernel order: every token slot
+        n_out = plan.n_real if use_out_perm else q.N
+    n_out = int(n_out)
     out = _out_tensor(q, n_out, out)
     lse_t = _lse_tensor(q, lse)
     qv, kv, vv = q.view(), k.view(), v.view()
