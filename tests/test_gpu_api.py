@@ -120,3 +120,22 @@ def test_strided_output_equals_contiguous(gpu_lib, recipe, causal):
     assert got.stride() == (N * H * d, d, H * d, 1)
     assert torch.equal(got, ref)
     assert not torch.isnan(buf).any()
+
+
+def test_sta_kernel_order_output_on_a_padded_grid(gpu_lib):
+    """attention_sta without the output permutation returns every token slot
+    of the padded grid in the kernel's tile-major order; its real rows equal
+    the caller-order output bit for bit."""
+    from precision_attention_block_amd import api
+    grid, real, tile, window = (4, 16, 16), (3, 15, 16), (2, 8, 8), (1, 3, 3)
+    hp = gpu_lib.sta_plan(grid, real, tile, window)
+    dp = gpu_lib.DevicePlan(hp, "cuda")
+    _, ts = _inputs(1, 2, int(np.prod(real)), 128, 92, torch.bfloat16, True)
+    qq, kq, vq = api.quantize_qkv(*(t.cuda() for t in ts), "fp8", hp.tile_tokens, dp.perm, hp.n_tokens)
+    caller = gpu_lib.attention_sta(qq, kq, vq, dp)
+    kernel = gpu_lib.attention_sta(qq, kq, vq, dp, use_out_perm=False)
+    torch.cuda.synchronize()
+    assert kernel.shape[2] == hp.n_tokens > caller.shape[2] == hp.n_real
+    perm = dp.perm.cpu().numpy()
+    live = np.nonzero(perm >= 0)[0]
+    assert torch.equal(kernel[:, :, live].cpu(), caller[:, :, perm[live]].cpu())
