@@ -41,7 +41,6 @@ DEFAULT_CONFIG = "dense_mxfp4_16k"
 PEAK_FP8 = 5000.0
 PEAK_FP4 = 10100.0
 PEAK_BF16 = 2500.0
-PEAK_BF16 = 2500.0
 # sources that define the attention kernel's code; a counter summary is valid
 # only for the sources it was taken on
 KERNEL_SOURCES = ("attention.hip", "pab_device.h", "pab_internal.h", "pab_lds.h")
@@ -130,13 +129,16 @@ class GpuPath:
                                      cfg.window if cfg.window else (99, 99, 99))
             self.dplan = lib.DevicePlan(self.plan, dev)
         self.out = torch.empty((cfg.B, cfg.H, cfg.n_real, cfg.d), dtype=torch.float32, device=dev)
+        self.q_operand = False
 
     def quantize(self):
         cfg, lib = self.cfg, self.lib
         perm = self.dplan.perm if self.dplan is not None else None
         n_out = cfg.n_kernel
         if cfg.recipe == "fp8":
-            qq = lib.quantize(self.q, "fp8_block", cfg.blk, perm, n_out)
+            # the forward reads K's bf16 operand copy and decodes Q's codes itself;
+            # the backward reads both copies
+            qq = lib.quantize(self.q, "fp8_block", cfg.blk, perm, n_out, operand=self.q_operand)
             kq = lib.quantize(self.k, "fp8_block", cfg.blk, perm, n_out)
         else:
             qq = lib.quantize(self.q, "mxfp4", None, perm, n_out)
@@ -187,6 +189,7 @@ def time_backward(cfg, path, steps, warmup):
     bf16 dO; returns per-call milliseconds."""
     import torch
     lib = path.lib
+    path.q_operand = True
     qq, kq, vq = path.quantize()
     causal = cfg.mode == "causal"
     sta = cfg.mode == "sta"

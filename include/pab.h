@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PAB_ABI_VERSION 7
+#define PAB_ABI_VERSION 8
 #define PAB_TOKEN_ALIGN 128  /* query tile of the attention kernel */
 #define PAB_MAX_TAU 8        /* largest softmax rescale threshold (log2 units) */
 
@@ -123,8 +123,9 @@ pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, in
  *                       (blocks holding no token below n_out get scale 1);
  *                       operand (if not NULL) bfloat16 [B, H, n_alloc, d]: the
  *                       exact value decode(code) of every code (not divided by
- *                       the scale) - the attention kernel multiplies Q and K
- *                       in this form, see pab_attention_dense.
+ *                       the scale) - the attention kernel reads K in this
+ *                       form, see pab_attention_dense; Q needs it only for
+ *                       the backward calls.
  *  PAB_FP8_CHANNEL:     codes uint8 [B, H, d, n_alloc] - transposed, and inside
  *                       every 64-token group the token t = 32a + 8b + 4g + c
  *                       (a < 2, b < 4, g < 2, c < 4) is stored at position
@@ -154,7 +155,9 @@ pab_status pab_quantize(const void* x, pab_dtype in_dt, const int64_t shape[4],
 typedef struct {
   const void* codes;
   const void* scales;
-  const void* operand;   /* PAB_FP8_TOKEN_BLOCK: the bf16 operand copy (required) */
+  const void* operand;   /* PAB_FP8_TOKEN_BLOCK: the bf16 operand copy; required for K,
+                            and for Q and K in the backward calls; the forward calls
+                            do not read Q's (NULL allowed) */
   pab_recipe recipe;
   int block_tokens;      /* PAB_FP8_TOKEN_BLOCK only */
   int64_t B, H, N, d;    /* N = tokens (n_out of pab_quantize) */
@@ -171,8 +174,8 @@ typedef struct {
  * order (causal: keys j <= i, top-left aligned) and keeps the running max m,
  * the sum l of the unquantised P and the accumulator of P~ V in fp32.
  * Q K^T of the FP8 recipe is summed from the exact products of the decoded
- * E4M3 values (the bf16 operand copies) with fp32 accumulation; P~ V uses the
- * FP8 matrix instructions.
+ * E4M3 values (K's bf16 operand copy; Q's codes are decoded in registers) with
+ * fp32 accumulation; P~ V uses the FP8 matrix instructions.
  * O[i,c] = acc[i,c] / (448 l_i) / s_V[c]; a row with no valid key gives 0.
  * FP4 P.V (V in PAB_MXFP4_V) [FV §1, FP4 attention]: P is requantised to
  * MXFP4 instead, per query row and per 32 consecutive keys of the tile, by the

@@ -9,11 +9,14 @@ this module itself never computes attention another way."""
 from . import binding as B
 
 
-def quantize_qkv(q, k, v, recipe="fp8", block_tokens=128, perm=None, n_out=None):
+def quantize_qkv(q, k, v, recipe="fp8", block_tokens=128, perm=None, n_out=None,
+                 q_operand=False):
     """recipe: "fp8" (Q/K FP8 per block), "mxfp4" (Q/K MXFP4) or "mxfp4_pv"
-    (Q/K MXFP4 and V MXFP4 along tokens: both products in FP4)."""
+    (Q/K MXFP4 and V MXFP4 along tokens: both products in FP4).
+    q_operand: also write Q's bf16 operand copy (FP8), which the backward
+    reads; the forward decodes Q's codes itself."""
     if recipe == "fp8":
-        qq = B.quantize(q, "fp8_block", block_tokens, perm, n_out)
+        qq = B.quantize(q, "fp8_block", block_tokens, perm, n_out, operand=q_operand)
         kq = B.quantize(k, "fp8_block", block_tokens, perm, n_out)
     elif recipe in ("mxfp4", "mxfp4_pv"):
         qq = B.quantize(q, "mxfp4", None, perm, n_out)
@@ -24,16 +27,20 @@ def quantize_qkv(q, k, v, recipe="fp8", block_tokens=128, perm=None, n_out=None)
     return qq, kq, vq
 
 
-def attention(q, k, v, recipe="fp8", block_tokens=128, causal=False, sm_scale=None, sta=None,
+def attention(q, k, v, recipe="fp8", block_tokens=None, causal=False, sm_scale=None, sta=None,
               check_finite=False, tau=0):
     """q, k, v: CUDA tensors [B, H, N, d] (float32 or bfloat16, any strides with
     unit channel stride; a packed qkv [B, N, 3, H, d] can be passed as three
     permuted views).  sta: None, or a binding.DevicePlan for sliding-tile
     attention over tokens given in raster order of the plan's real grid.
+    block_tokens: tokens per FP8 Q/K scale block; None gives one scale per 3D
+    tile on the sliding-tile path (the FPSAttention page, §2.3 and §3.1: one
+    tile serves both the quantisation and the sparsity) and 128 tokens on the
+    dense path.
     tau: softmax rescale threshold (0 = rescale on every rise of the maximum).
     Returns float32 [B, H, N, d]."""
     if sta is None:
-        qq, kq, vq = quantize_qkv(q, k, v, recipe, block_tokens)
+        qq, kq, vq = quantize_qkv(q, k, v, recipe, 128 if block_tokens is None else block_tokens)
         out = B.attention_dense(qq, kq, vq, causal=causal, sm_scale=sm_scale, tau=tau)
     else:
         if causal:
@@ -60,7 +67,7 @@ def _attention_function():
 
         @staticmethod
         def forward(ctx, q, k, v, recipe, block_tokens, causal, sm_scale):
-            qq, kq, vq = quantize_qkv(q, k, v, recipe, block_tokens)
+            qq, kq, vq = quantize_qkv(q, k, v, recipe, block_tokens, q_operand=True)
             out, lse = B.attention_dense(qq, kq, vq, causal=causal, sm_scale=sm_scale, lse=True)
             ctx.ops = (qq, kq, vq)
             ctx.causal, ctx.sm_scale = causal, sm_scale

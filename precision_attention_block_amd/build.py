@@ -1,4 +1,6 @@
-"""Builds libpab.so (HIP kernels + C ABI) for gfx950 in the package directory.
+"""Builds libpab.so (HIP kernels + C ABI) for gfx950 in the package directory,
+and libpab_probe.so, the matrix-instruction probe that tests use
+(include/pab_probe.h).
 
     python -m precision_attention_block_amd.build
 
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpab.so")
 SOURCES = ["api.cpp", "quant.hip", "attention.hip", "attention_bwd.hip"]
+PROBE_LIB = os.path.join(PKG, "libpab_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 # The attention kernel's inputs are finite by contract (scores, exponentials
 # and maxima never see NaN), so its fmax needs no NaN-quieting of operands.
 EXTRA = {"attention.hip": ["-fno-honor-nans"]}
@@ -37,6 +41,13 @@ def flags():
 
 
 def build(verbose=False, out=LIB):
+    """Builds libpab.so (at `out`) and libpab_probe.so."""
+    _build_lib(SOURCES, out, verbose)
+    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose)
+    return out
+
+
+def _build_lib(sources, out, verbose):
     hipcc = _hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -55,8 +66,8 @@ def build(verbose=False, out=LIB):
             print(msg, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(max_workers=len(sources)) as ex:
+        objs = list(ex.map(compile_one, sources))
     tmp = out + ".tmp"
     cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -47,8 +47,11 @@ constexpr int64_t kMaxAttnRows = (int64_t)1 << 31;     // B*H*n_alloc (exclusive
 constexpr int64_t kMaxGridY = 65536;                   // B*H of the quantiser and backward grids (y)
 constexpr int64_t kMaxQuantTokens = (int64_t)1 << 27;  // n_out: up to 16 work-items per token slot
 
-// Validates a quantised operand view; `role` 0 = Q/K, 1 = V.
-pab_status check_view(const pab_qview* v, int role) {
+// Validates a quantised operand view; `role` 0 = Q/K, 1 = V.  An FP8 Q/K
+// view must carry its bf16 operand copy when `need_operand` is set (the
+// forward reads K's copy and converts Q's codes itself; the backward reads
+// both copies).
+pab_status check_view(const pab_qview* v, int role, bool need_operand = true) {
   if (!v || !v->codes || !v->scales) return PAB_INVALID_ARG;
   if (v->B < 1 || v->H < 1 || v->N < 1 || v->d < 1) return PAB_INVALID_ARG;
   if (v->B * v->H > (int64_t)1 << 24 || v->N > kMaxAttnTokens) return PAB_UNSUPPORTED;
@@ -63,7 +66,8 @@ pab_status check_view(const pab_qview* v, int role) {
   if (v->recipe == PAB_FP8_TOKEN_BLOCK) {
     if (v->d != 64 && v->d != 128) return PAB_UNSUPPORTED;
     if (v->block_tokens < 16 || v->block_tokens > 16384 || v->block_tokens % 16) return PAB_INVALID_ARG;
-    if (!v->operand || !aligned(v->operand, 16)) return PAB_INVALID_ARG;
+    if (need_operand && !v->operand) return PAB_INVALID_ARG;
+    if (v->operand && !aligned(v->operand, 16)) return PAB_INVALID_ARG;
     return PAB_OK;
   }
   if (v->recipe == PAB_MXFP4_D32) return v->d == 128 ? PAB_OK : PAB_UNSUPPORTED;
@@ -88,7 +92,7 @@ pab_status fill_attn_args(const pab_qview* q, const pab_qview* k, const pab_qvie
                           int64_t n_out_tokens, float* out, const int64_t out_strides[4],
                           pab::AttnArgs& a) {
   pab_status s;
-  if ((s = check_view(q, 0)) != PAB_OK) return s;
+  if ((s = check_view(q, 0, false)) != PAB_OK) return s;
   if ((s = check_view(k, 0)) != PAB_OK) return s;
   if ((s = check_view(v, 1)) != PAB_OK) return s;
   if (q->recipe != k->recipe) return PAB_INVALID_ARG;
@@ -111,7 +115,6 @@ pab_status fill_attn_args(const pab_qview* q, const pab_qview* k, const pab_qvie
   std::memset(&a, 0, sizeof(a));
   a.q = static_cast<const uint8_t*>(q->codes);
   a.k = static_cast<const uint8_t*>(k->codes);
-  a.q16 = static_cast<const uint8_t*>(q->operand);
   a.k16 = static_cast<const uint8_t*>(k->operand);
   a.vt = static_cast<const uint8_t*>(v->codes);
   if (mx) {

@@ -165,6 +165,24 @@ __device__ inline void issue_aux(uint8_t* abuf, const HeadBuffers& hb, int ks, i
                                              (ks / hb.blk_k) * 4, 0, 0);
 }
 
+// The bf16 operand of S = K Q^T for one lane of the FP8 recipe, converted in
+// registers from the lane's QI chunks of 8 consecutive E4M3 codes (channels
+// 8 (QI lg + i) .. + 7 at step i): every E4M3 value is exact in bf16, so this
+// equals the decoded value of each code.
+template <int QI>
+__device__ inline void load_q_codes(const uint8_t* p, v8s (&qop)[QI]) {
+#pragma unroll
+  for (int i = 0; i < QI; i += 2) {
+    const uint4 c = *reinterpret_cast<const uint4*>(p + 8 * i);   // chunks i and i + 1
+    const uint4 lo = make_uint4(e4m3_bf16x2<false>(c.x), e4m3_bf16x2<true>(c.x),
+                                e4m3_bf16x2<false>(c.y), e4m3_bf16x2<true>(c.y));
+    const uint4 hi = make_uint4(e4m3_bf16x2<false>(c.z), e4m3_bf16x2<true>(c.z),
+                                e4m3_bf16x2<false>(c.w), e4m3_bf16x2<true>(c.w));
+    qop[i] = __builtin_bit_cast(v8s, lo);
+    qop[i + 1] = __builtin_bit_cast(v8s, hi);
+  }
+}
+
 __device__ inline v8i make_v8(uint4 lo, uint4 hi) {
   v8i r;
   r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
@@ -290,10 +308,7 @@ __global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
       }
       cq = a.sm_log2;
     } else {
-      const uint8_t* qp = a.q16 + qrow * (2 * D) + 16 * QI * lg;
-#pragma unroll
-      for (int i = 0; i < QI; ++i)
-        qop16[i] = __builtin_bit_cast(v8s, *reinterpret_cast<const uint4*>(qp + 16 * i));
+      load_q_codes<QI>(a.q + qrow * D + 8 * QI * lg, qop16);
       cq = a.sm_log2 / a.q_scale[(int64_t)bh * a.nblk_q + myq / a.blk_q];
     }
   }
@@ -934,14 +949,13 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
         qop8[i] = r;
       }
     } else {
-      const uint8_t* qp = a.q16 + qrow * (2 * D) + 16 * QI * lg;
+      if (q_live) {
+        load_q_codes<QI>(a.q + qrow * D + 8 * QI * lg, qop16);
+        cq = a.sm_log2 / a.q_scale[(int64_t)bh * a.nblk_q + myq / a.blk_q];
+      } else {
 #pragma unroll
-      for (int i = 0; i < QI; ++i) {
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (q_live) x = *reinterpret_cast<const uint4*>(qp + 16 * i);
-        qop16[i] = __builtin_bit_cast(v8s, x);
+        for (int i = 0; i < QI; ++i) qop16[i] = __builtin_bit_cast(v8s, make_uint4(0u, 0u, 0u, 0u));
       }
-      if (q_live) cq = a.sm_log2 / a.q_scale[(int64_t)bh * a.nblk_q + myq / a.blk_q];
     }
   }
 

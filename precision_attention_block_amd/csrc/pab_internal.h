@@ -25,10 +25,9 @@ struct QuantArgs {
 
 // Arguments of the attention kernel.
 struct AttnArgs {
-  const uint8_t* q;       // MXFP4 codes [BH][n_alloc][d/2]
+  const uint8_t* q;       // MXFP4 codes [BH][n_alloc][d/2]; FP8 E4M3 codes [BH][n_alloc][d]
   const uint8_t* k;
-  const uint8_t* q16;     // FP8 recipe: bf16 values of the E4M3 codes [BH][n_alloc][d]
-  const uint8_t* k16;
+  const uint8_t* k16;     // FP8 recipe: bf16 values of K's E4M3 codes [BH][n_alloc][d]
   const uint8_t* vt;      // FP8 V^T [BH][d][n_alloc], operand-ordered per 64 tokens;
                           // FP4 P.V: MXFP4 V^T [BH][d][n_alloc/2]
   const uint8_t* v_mx;    // FP4 P.V: E8M0 V scales [BH][n_alloc/32][d] (channels interleaved)

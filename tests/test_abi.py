@@ -26,7 +26,22 @@ def test_exports_every_declared_symbol(B):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(B.lib(), name), name
-    assert B.lib().pab_abi_version() == 7
+    assert B.lib().pab_abi_version() == 8
+
+
+def test_probe_library_exports_its_header():
+    """libpab_probe.so (the matrix-instruction probe the GPU tests use) loads
+    and exports what include/pab_probe.h declares."""
+    header = open(os.path.join(ROOT, "include", "pab_probe.h")).read()
+    declared = set(re.findall(r"\b(pab_[a-z0-9_]+)\s*\(", header))
+    assert declared == {"pab_probe_mfma_e4m3"}
+    L = ctypes.CDLL(os.path.join(ROOT, "precision_attention_block_amd", "libpab_probe.so"))
+    for name in declared:
+        assert hasattr(L, name), name
+    f = ctypes.c_void_p(4096)
+    L.pab_probe_mfma_e4m3.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p]
+    assert L.pab_probe_mfma_e4m3(f, f, f, 2, None) == 1                      # unknown kind
+    assert L.pab_probe_mfma_e4m3(f, ctypes.c_void_p(4100), f, 0, None) == 1  # misaligned
 
 
 def test_token_alloc_and_info(B):
@@ -110,7 +125,8 @@ def test_attention_validation_without_device(B):
     assert dense(qv, kv, mk(0)) == B.PAB_INVALID_ARG          # V with the Q/K recipe
     assert dense(qv, mk(2), vv) == B.PAB_INVALID_ARG          # mixed Q/K recipes
     assert dense(qv, mk(0, n=300), vv) == B.PAB_INVALID_ARG   # shape mismatch
-    assert dense(mk(0, op=0), kv, vv) == B.PAB_INVALID_ARG    # FP8 Q without operand copy
+    assert dense(qv, mk(0, op=0), vv) == B.PAB_INVALID_ARG    # FP8 K without operand copy
+    assert dense(mk(0, op=fake + 2), kv, vv) == B.PAB_INVALID_ARG   # misaligned Q operand copy
     assert dense(mk(0, d=96), mk(0, d=96), mk(1, d=96)) == B.PAB_UNSUPPORTED
     assert dense(qv, kv, vv, n_out=100) == B.PAB_INVALID_ARG  # output too small
     assert dense(qv, kv, vv, sm=float("nan")) == B.PAB_INVALID_ARG

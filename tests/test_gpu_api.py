@@ -75,7 +75,7 @@ def test_autograd_uses_the_library_backward(gpu_lib, recipe, causal):
     dout = torch.from_numpy(rng.standard_normal((B, H, N, d)).astype(np.float32)).cuda()
     out = api.attention_autograd(q, k, v, recipe=recipe, block_tokens=64, causal=causal)
     out.backward(dout)
-    qq, kq, vq = api.quantize_qkv(q.detach(), k.detach(), v.detach(), recipe, 64)
+    qq, kq, vq = api.quantize_qkv(q.detach(), k.detach(), v.detach(), recipe, 64, q_operand=True)
     o2, lse = gpu_lib.attention_dense(qq, kq, vq, causal=causal, lse=True)
     grads = gpu_lib.attention_backward(qq, kq, vq, o2, dout, lse, causal=causal)
     torch.cuda.synchronize()
@@ -139,3 +139,24 @@ def test_sta_kernel_order_output_on_a_padded_grid(gpu_lib):
     perm = dp.perm.cpu().numpy()
     live = np.nonzero(perm >= 0)[0]
     assert torch.equal(kernel[:, :, live].cpu(), caller[:, :, perm[live]].cpu())
+
+
+@pytest.mark.parametrize("d,causal", [(128, False), (128, True), (64, False)])
+def test_fp8_forward_needs_no_q_operand(gpu_lib, d, causal):
+    """The forward decodes Q's E4M3 codes in registers: a Q view without its
+    bf16 operand copy is accepted and gives the output of a view with it, bit
+    for bit (ping-pong kernel for dense d = 128, 4-wave kernel otherwise)."""
+    x, ts = _inputs(1, 2, 700, d, 41, torch.bfloat16, True)
+    q, k, v = (t.cuda() for t in ts)
+    kq = gpu_lib.quantize(k, "fp8_block", 64)
+    vq = gpu_lib.quantize(v, "fp8_channel")
+    with_op = gpu_lib.quantize(q, "fp8_block", 64)
+    without = gpu_lib.quantize(q, "fp8_block", 64, operand=False)
+    assert without.operand is None and with_op.operand is not None
+    assert torch.equal(with_op.codes, without.codes) and torch.equal(with_op.scales, without.scales)
+    a = gpu_lib.attention_dense(with_op, kq, vq, causal=causal)
+    b = gpu_lib.attention_dense(without, kq, vq, causal=causal)
+    assert torch.equal(a, b)
+    _, bn = gpu_lib.attention_info("fp8_block", d, 1 if causal else 0)
+    ref = _oracle_dense(x, "fp8", 64, causal, 1 / np.sqrt(d), bn)
+    assert_close(b.cpu().numpy(), ref, "no Q operand d=%d causal=%s" % (d, causal))
