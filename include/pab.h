@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PAB_ABI_VERSION 8
+#define PAB_ABI_VERSION 9
 #define PAB_TOKEN_ALIGN 128  /* query tile of the attention kernel */
 #define PAB_MAX_TAU 8        /* largest softmax rescale threshold (log2 units) */
 
@@ -321,6 +321,36 @@ pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const 
                                   const int64_t dout_strides[4], const float* lse, float* dq,
                                   float* dk, float* dv, const int64_t grad_strides[4],
                                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Largest workspace (bytes) of pab_attention_backward_noalloc: the size of
+ * the library's own device array. */
+#define PAB_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+
+/*
+ * pab_attention_backward_noalloc - pab_attention_backward for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same gradients from the same
+ * kernels, with the workspace taken from a file-scope device array of
+ * PAB_NOALLOC_SCRATCH_BYTES inside the library instead of a caller buffer.
+ * Every argument but the workspace is as for pab_attention_backward.
+ * The array's address on a device is looked up once, at the first call on
+ * that device (the stream's device); the call itself allocates nothing.
+ * Each device holds one array for the life of the process, shared by every
+ * call on that device: calls that overlap in time on one device (on
+ * different streams, or from different threads) race on it and must be
+ * serialised by the caller.  The kernels write every workspace byte they
+ * read, so no state carries over between calls.
+ * PAB_UNSUPPORTED when the problem needs more than PAB_NOALLOC_SCRATCH_BYTES
+ * of workspace (pab_attention_backward_workspace gives the need), before any
+ * launch; PAB_HIP_ERROR if the address lookup fails.
+ */
+pab_status pab_attention_backward_noalloc(const pab_qview* q, const pab_qview* k,
+                                          const pab_qview* v, int causal, float sm_scale,
+                                          const uint8_t* kv_valid, const float* out,
+                                          const int64_t out_strides[4], const void* dout,
+                                          pab_dtype dout_dtype, const int64_t dout_strides[4],
+                                          const float* lse, float* dq, float* dk, float* dv,
+                                          const int64_t grad_strides[4], void* stream);
 
 /* Backward of sliding-tile attention (pab_attention_sta): the gradients of
  * pab_attention_backward, with key j visible to query i when the tile of j is

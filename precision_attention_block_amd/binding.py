@@ -23,7 +23,7 @@ EXPORTS = [
     "pab_attention_info", "pab_quantize", "pab_attention_dense", "pab_attention_sta",
     "pab_sta_plan", "pab_count_nonfinite", "pab_attention_backward_workspace",
     "pab_attention_backward", "pab_attention_sta_backward", "pab_attention_dense_tiles", "pab_key_tiles",
-    "pab_attention_sta_steps", "pab_sta_steps",
+    "pab_attention_sta_steps", "pab_sta_steps", "pab_attention_backward_noalloc",
 ]
 
 
@@ -91,6 +91,10 @@ def _lib():
         L.pab_attention_backward.argtypes = [ctypes.POINTER(QView)] * 3 + [
             ctypes.c_int, ctypes.c_float, vp, vp, i64p, vp, ctypes.c_int, i64p, vp, vp, vp, vp,
             i64p, vp, ctypes.c_int64, vp]
+        L.pab_attention_backward_noalloc.restype = ctypes.c_int
+        L.pab_attention_backward_noalloc.argtypes = [ctypes.POINTER(QView)] * 3 + [
+            ctypes.c_int, ctypes.c_float, vp, vp, i64p, vp, ctypes.c_int, i64p, vp, vp, vp, vp,
+            i64p, vp]
         L.pab_attention_sta_backward.restype = ctypes.c_int
         L.pab_attention_sta_backward.argtypes = [ctypes.POINTER(QView)] * 3 + [
             ctypes.c_float, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp, i64p, vp, ctypes.c_int, i64p,
@@ -316,6 +320,35 @@ def attention_backward(q, k, v, out, dout, lse, causal=False, sm_scale=None, kv_
         ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()), _i64(dq.stride()),
         ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(dev))
     _check(st, "pab_attention_backward")
+    return dq, dk, dv
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def attention_backward_noalloc(q, k, v, out, dout, lse, causal=False, sm_scale=None,
+                               kv_valid=None, grads=None):
+    """attention_backward without a workspace argument: the library takes it
+    from its own device array (pab_attention_backward_noalloc); the gradient
+    buffers are the caller's (allocated here when `grads` is None)."""
+    import torch
+    dev = out.device
+    if grads is None:
+        grads = tuple(torch.empty((q.B, q.H, q.N, q.d), dtype=torch.float32, device=dev)
+                      for _ in range(3))
+    dq, dk, dv = grads
+    if dk.stride() != dq.stride() or dv.stride() != dq.stride():
+        raise ValueError("dq, dk and dv must share strides")
+    dt = {torch.float32: PAB_F32, torch.bfloat16: PAB_BF16}[dout.dtype]
+    qv, kv, vv = q.view(), k.view(), v.view()
+    st = _lib().pab_attention_backward_noalloc(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), int(bool(causal)),
+        float(sm_scale or 0.0), ctypes.c_void_p(kv_valid.data_ptr() if kv_valid is not None else 0),
+        ctypes.c_void_p(out.data_ptr()), _i64(out.stride()), ctypes.c_void_p(dout.data_ptr()), dt,
+        _i64(dout.stride()), ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(dq.data_ptr()),
+        ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()), _i64(dq.stride()),
+        _stream(dev))
+    _check(st, "pab_attention_backward_noalloc")
     return dq, dk, dv
 
 

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <vector>
 #include <algorithm>
+#include <mutex>
 #include <numeric>
 
 #include "../../include/pab.h"
@@ -409,7 +410,8 @@ static pab_status backward_impl(const pab_qview* q, const pab_qview* k, const pa
                                 const void* dout, pab_dtype dout_dtype,
                                 const int64_t dout_strides[4], const float* lse, float* dq,
                                 float* dk, float* dv, const int64_t grad_strides[4],
-                                void* workspace, int64_t workspace_bytes, void* stream) {
+                                void* workspace, int64_t workspace_bytes, void* stream,
+                                bool launch = true) {
   if (empty_views(q, k, v)) return PAB_OK;
   pab_status s;
   if ((s = check_view(q, 0)) != PAB_OK) return s;
@@ -439,6 +441,7 @@ static pab_status backward_impl(const pab_qview* q, const pab_qview* k, const pa
   const int64_t BH = q->B * q->H, n_alloc = round_up(q->N, PAB_TOKEN_ALIGN);
   int64_t off[13];
   if (workspace_bytes < pab::bwd_workspace_layout(BH, n_alloc, q->d, off)) return PAB_INVALID_ARG;
+  if (!launch) return PAB_OK;   // validation only
 
   pab::BwdArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -523,6 +526,72 @@ pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const 
   return backward_impl(q, k, v, causal, sm_scale, kv_valid, nullptr, nullptr, 0, out, out_strides,
                        dout, dout_dtype, dout_strides, lse, dq, dk, dv, grad_strides, workspace,
                        workspace_bytes, stream);
+}
+
+namespace {
+
+// Workspace of pab_attention_backward_noalloc.  In host code the array's name
+// stands for a host-side shadow, not a device address: the device address of
+// each device's copy comes from hipGetSymbolAddress and is the only form that
+// reaches a kernel.
+static __device__ __align__(256) uint8_t scratch[PAB_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the device of `st`, looked up once per device
+// with that device current.
+pab_status scratch_address(hipStream_t st, void** out) {
+  int dev = 0;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, st);
+  if (dev < 0 || dev >= kMaxScratchDevices) return PAB_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status(e, st);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, st);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, st);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PAB_OK;
+}
+
+}  // namespace
+
+pab_status pab_attention_backward_noalloc(const pab_qview* q, const pab_qview* k,
+                                          const pab_qview* v, int causal, float sm_scale,
+                                          const uint8_t* kv_valid, const float* out,
+                                          const int64_t out_strides[4], const void* dout,
+                                          pab_dtype dout_dtype, const int64_t dout_strides[4],
+                                          const float* lse, float* dq, float* dk, float* dv,
+                                          const int64_t grad_strides[4], void* stream) {
+  if (empty_views(q, k, v)) return PAB_OK;
+  if (!q) return PAB_INVALID_ARG;
+  const int64_t need = pab_attention_backward_workspace(q->B, q->H, q->N, q->d);
+  if (need < 0) return PAB_INVALID_ARG;
+  if (need > PAB_NOALLOC_SCRATCH_BYTES) return PAB_UNSUPPORTED;
+  // every argument is checked (with a stand-in workspace address) before the
+  // device is touched
+  pab_status s = backward_impl(q, k, v, causal, sm_scale, kv_valid, nullptr, nullptr, 0, out,
+                               out_strides, dout, dout_dtype, dout_strides, lse, dq, dk, dv,
+                               grad_strides, reinterpret_cast<void*>(256), PAB_NOALLOC_SCRATCH_BYTES,
+                               stream, false);
+  if (s != PAB_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((s = scratch_address(st, &ws)) != PAB_OK) return s;
+  return backward_impl(q, k, v, causal, sm_scale, kv_valid, nullptr, nullptr, 0, out, out_strides,
+                       dout, dout_dtype, dout_strides, lse, dq, dk, dv, grad_strides, ws,
+                       PAB_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 pab_status pab_attention_sta_backward(const pab_qview* q, const pab_qview* k, const pab_qview* v,

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(B):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(B.lib(), name), name
-    assert B.lib().pab_abi_version() == 8
+    assert B.lib().pab_abi_version() == 9
 
 
 def test_probe_library_exports_its_header():
@@ -175,6 +175,33 @@ def test_backward_validation_without_device(B):
     assert bwd(k=mk(2)) == B.PAB_INVALID_ARG                          # mixed Q/K recipes
     assert bwd(q=mk(0, op=0)) == B.PAB_INVALID_ARG                    # FP8 Q without operand copy
     assert L.pab_last_hip_error() == 0
+
+
+def test_backward_noalloc_validation_without_device(B):
+    """pab_attention_backward_noalloc checks its size limit and every argument
+    before it touches a device."""
+    L = B.lib()
+    fake = 4096
+    mk = lambda recipe, n=256, h=2, op=fake: B.QView(fake, fake, op, recipe, 128, 1, h, n, 128)
+    st = B._i64([2 * 256 * 128, 256 * 128, 128, 1])
+    null = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(fake)
+
+    def call(q, k, v, lse=f):
+        return L.pab_attention_backward_noalloc(
+            ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, 0.0, null, f, st, f, B.PAB_F32, st,
+            lse, f, f, f, st, null)
+    # the workspace of H = 64 heads of 8192 tokens is far above the array's 32 MiB
+    big = [mk(0, 8192, 64), mk(0, 8192, 64), mk(1, 8192, 64)]
+    assert L.pab_attention_backward_workspace(1, 64, 8192, 128) > B.NOALLOC_SCRATCH_BYTES
+    assert call(*big) == B.PAB_UNSUPPORTED
+    assert call(mk(0), mk(0), mk(1), lse=null) == B.PAB_INVALID_ARG
+    assert call(mk(0, op=0), mk(0), mk(1)) == B.PAB_INVALID_ARG       # FP8 Q without operand copy
+    assert call(mk(0), mk(2), mk(1)) == B.PAB_INVALID_ARG             # mixed Q/K recipes
+    assert L.pab_last_hip_error() == 0
+    header = open(os.path.join(ROOT, "include", "pab.h")).read()
+    assert "#define PAB_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)" in header
+    assert B.NOALLOC_SCRATCH_BYTES == 32 << 20
 
 
 def test_key_tiles_helper(B):
