@@ -255,23 +255,33 @@ def test_backward_custom_softmax_scale(gpu_lib, sm):
         _grads_close([g[0, h] for g in got], ref, bounds, "sm %g h%d" % (sm, h))
 
 
-def test_sta_backward_parity(gpu_lib):
+@pytest.mark.parametrize("case", [
+    dict(grid=(2, 32, 32), real=(2, 30, 29), tile=(2, 8, 8), H=2, recipe="fp8", blk=None),
+    # (6, 8, 8) tiles of 384 tokens, as the sliding-tile workloads use: a
+    # workgroup's 128 keys or queries are a third of a window tile
+    dict(grid=(6, 16, 24), real=(5, 15, 22), tile=(6, 8, 8), H=1, recipe="fp8", blk=None),
+    # FP8 blocks of 16 tokens: the Q and K scales vary inside a 32-token step
+    dict(grid=(2, 32, 32), real=(2, 30, 29), tile=(2, 8, 8), H=1, recipe="fp8", blk=16),
+    dict(grid=(6, 16, 24), real=(5, 15, 22), tile=(6, 8, 8), H=1, recipe="mxfp4", blk=None),
+], ids=["fp8_tile128", "fp8_tile384", "fp8_blk16", "mxfp4_tile384"])
+def test_sta_backward_parity(gpu_lib, case):
     """Backward of sliding-tile attention (pab_attention_sta_backward) on a
-    padded grid: 16 tiles of 128 tokens, window (1, 3, 3), so a tile sees at
-    most 9 of them.  Both sides take the oracle's per-tile forward (kernel
-    token order); the reference is the oracle backward with the token-level
-    mask "tile of j in the window of the tile of i, and key j valid", under
-    the element-wise gate."""
+    padded grid with window (1, 3, 3), so a tile sees at most 9 of the others.
+    Both sides take the oracle's per-tile forward (kernel token order); the
+    reference is the oracle backward with the token-level mask "tile of j in
+    the window of the tile of i, and key j valid", under the element-wise
+    gate.  FP8 scale blocks are one tile unless the case sets blk."""
     from oracle import sta as OS
-    grid, real, tile, window = (2, 32, 32), (2, 30, 29), (2, 8, 8), (1, 3, 3)
+    grid, real, tile, window = case["grid"], case["real"], case["tile"], (1, 3, 3)
     hp = gpu_lib.sta_plan(grid, real, tile, window)
     dp = gpu_lib.DevicePlan(hp)
     op = OS.plan(grid, real, tile, window)
-    B, H, N, d, tt = 1, 2, hp.n_tokens, 128, hp.tile_tokens
+    B, H, N, d, tt = 1, case["H"], hp.n_tokens, 128, hp.tile_tokens
+    recipe, blk = case["recipe"], case["blk"] or hp.tile_tokens
     x, ts, do = _inputs(B, H, N, d, 67)
     sm = 1 / np.sqrt(d)
-    _, bn = gpu_lib.attention_info("fp8_block", d, 2)
-    ops = oracle_operands(*x, "fp8", tt)
+    _, bn = gpu_lib.attention_info("mxfp4" if recipe == "mxfp4" else "fp8_block", d, 2)
+    ops = oracle_operands(*x, recipe, blk)
     o_ref = np.zeros((B, H, N, d), np.float32)
     lse_ref = np.zeros((B, H, N), np.float32)
     for h in range(H):
@@ -287,8 +297,9 @@ def test_sta_backward_parity(gpu_lib):
         see[u, op.win_idx[op.win_off[u]:op.win_off[u + 1]]] = True
     assert np.array_equal(see, see.T) and not see.all()
     mask = see[tiles_of][:, tiles_of] & op.kv_valid.astype(bool)[None, :]
-    q, k, v = _quantize(gpu_lib, [t.cuda() for t in ts], "fp8", tt)
-    print("sta backward: %d tiles, %d pairs, N = %d" % (op.n_tiles, int(see.sum()), N), flush=True)
+    q, k, v = _quantize(gpu_lib, [t.cuda() for t in ts], recipe, blk)
+    print("sta backward %s: %d tiles of %d tokens, %d pairs, N = %d" % (
+        recipe, op.n_tiles, tt, int(see.sum()), N), flush=True)
     dq, dk, dv = gpu_lib.attention_sta_backward(q, k, v, dp, torch.from_numpy(o_ref).cuda(), do.cuda(),
                                                 torch.from_numpy(lse_ref).cuda())
     torch.cuda.synchronize()
@@ -300,4 +311,4 @@ def test_sta_backward_parity(gpu_lib):
         ref = OB.backward_core(qh, kh, vh, o_ref[0, h], do_h[0, h], lse_ref[0, h], sm, mask)
         bounds = _error_bounds(qo, ko, vo, o_ref[0, h].astype(np.float64), do_h[0, h],
                                lse_ref[0, h].astype(np.float64), sm, mask)
-        _grads_close([g[0, h] for g in got], ref, bounds, "sta h%d" % h)
+        _grads_close([g[0, h] for g in got], ref, bounds, "sta %s h%d" % (recipe, h))
