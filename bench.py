@@ -13,7 +13,8 @@ algorithmic FLOPs / time, with FLOPs = 4 N^2 d H for dense attention (causal:
 4 d H N(N+1)/2; sliding-tile and padded grids: only real query-key pairs that
 are computed).  `value` uses the whole step (quantisers + attention);
 `roofline` is for the attention kernel alone, timed with events on the stream
-it runs on.  `cpu_baseline` times the CPU oracle on a bounded sample.
+it runs on.  `cpu_baseline` times the CPU oracle: its quantisers on the full
+tensors and its attention on 4096 seeded (head, query) rows.
 
 `roofline.traffic` (HBM bytes per attention launch) comes from the committed
 counter summary profiles/attention_<workload>_counters.md, made by two
@@ -259,67 +260,109 @@ def backward_main(args, cfg, path):
     print(json.dumps(result))
 
 
-def cpu_baseline(cfg, x, plan, bn, budget_s=15.0):
-    """The oracle (as it stands) on a bounded sample: quantise one head's Q, K,
-    V and run the recipe for a set of query rows of that head; scaled to the
-    metric's unit with the same FLOP formula (computed query-key pairs)."""
+_ORACLE_PLAN = {}
+
+
+def _oracle_plan_cached(cfg):
+    if cfg.name not in _ORACLE_PLAN:
+        _ORACLE_PLAN[cfg.name] = _oracle_plan(cfg)
+    return _ORACLE_PLAN[cfg.name]
+
+
+def _oracle_quantize_head(job):
+    """Worker: the oracle's quantisers on one head's full Q, K and V (after the
+    3D token reorder on grid workloads); returns the operands and the time."""
     from oracle import attention as OA
     from oracle import quant as OQ
     from oracle import sta as OS
-    cores = len(os.sched_getaffinity(0))
-    q, k, v = (x[n][0, 0] for n in ("q", "k", "v"))   # one (b, h) slice, raster order
+    name, q, k, v = job
+    cfg = CONFIGS[name]
     t0 = time.perf_counter()
-    if plan is not None:
-        q, k, v = (OS.gather_tokens(a[None], plan.perm)[0] for a in (q, k, v))
+    if cfg.grid is not None:
+        perm = _oracle_plan_cached(cfg).perm
+        q, k, v = (OS.gather_tokens(a[None], perm)[0] for a in (q, k, v))
     if cfg.recipe == "fp8":
-        qc, qs = OQ.fp8_block_quantize(q, cfg.blk)
-        kc, ks = OQ.fp8_block_quantize(k, cfg.blk)
-        qo, ko = OA.Operand("fp8_block", qc, qs, cfg.blk), OA.Operand("fp8_block", kc, ks, cfg.blk)
+        qo = OA.Operand("fp8_block", *OQ.fp8_block_quantize(q, cfg.blk), cfg.blk)
+        ko = OA.Operand("fp8_block", *OQ.fp8_block_quantize(k, cfg.blk), cfg.blk)
     else:
-        qc, qe = OQ.mxfp4_quantize(q)
-        kc, ke = OQ.mxfp4_quantize(k)
-        qo, ko = OA.Operand("mxfp4", qc, qe), OA.Operand("mxfp4", kc, ke)
+        qo = OA.Operand("mxfp4", *OQ.mxfp4_quantize(q))
+        ko = OA.Operand("mxfp4", *OQ.mxfp4_quantize(k))
     if cfg.recipe == "mxfp4_pv":
-        vc, ve = OQ.mxfp4_token_quantize(v)
-        vo = OA.Operand("mxfp4_tokens", vc, ve)
+        vo = OA.Operand("mxfp4_tokens", *OQ.mxfp4_token_quantize(v))
     else:
-        vc, vs = OQ.fp8_channel_quantize(v)
-        vo = OA.Operand("fp8_channel", vc, vs)
-    t_quant = time.perf_counter() - t0
+        vo = OA.Operand("fp8_channel", *OQ.fp8_channel_quantize(v))
+    return (qo, ko, vo), time.perf_counter() - t0
+
+
+def _oracle_rows(job):
+    """Worker: the oracle recipe for one head's sampled query rows (raster
+    tokens); returns the computed (query, key) pairs and the time."""
+    from oracle import attention as OA
+    from oracle import sta as OS
+    name, ops, tokens, bn = job
+    cfg = CONFIGS[name]
+    qo, ko, vo = ops
     sm = 1.0 / np.sqrt(cfg.d)
-    n = q.shape[0]
-    kv_valid = plan.kv_valid if plan is not None else None
-    rows_done, pairs, t_att = 0, 0.0, 0.0
-    chunk = 64
-    rng = np.random.default_rng(1000 * cfg.index + 6)
-    while t_att < budget_s and rows_done < n:
-        if cfg.mode == "sta":
-            u = int(rng.integers(plan.n_tiles))
-            rows = np.arange(u * plan.tile_tokens, u * plan.tile_tokens + chunk)
-            kb = OS.key_blocks_for_tile(plan, u, bn)
-            t1 = time.perf_counter()
-            OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm, bn=bn, kv_valid=kv_valid, key_blocks=kb)
-            t_att += time.perf_counter() - t1
+    t0 = time.perf_counter()
+    pairs = 0.0
+    if cfg.grid is not None:
+        plan = _oracle_plan_cached(cfg)
+        ok = plan.perm >= 0
+        inv = np.empty(int(ok.sum()), np.int64)
+        inv[plan.perm[ok]] = np.nonzero(ok)[0]
+        rows = inv[np.asarray(tokens, np.int64)]
+        tiles = rows // plan.tile_tokens
+        for u in np.unique(tiles):
+            sel = rows[tiles == u]
+            kb = OS.key_blocks_for_tile(plan, int(u), bn)
+            OA.recipe_attention(qo, ko, vo, sel, sm_scale=sm, bn=bn, kv_valid=plan.kv_valid,
+                                key_blocks=kb)
             keys = plan.kv_valid[np.concatenate([np.arange(s, s + bn) for s in kb])].sum()
-            pairs += float((plan.kv_valid[rows] > 0).sum()) * keys
-        else:
-            r0 = int(rng.integers(0, max(1, n - chunk)))
-            rows = np.arange(r0, min(n, r0 + chunk))
-            t1 = time.perf_counter()
-            OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm, bn=bn, causal=cfg.mode == "causal",
-                                kv_valid=kv_valid)
-            t_att += time.perf_counter() - t1
-            if cfg.mode == "causal":
-                pairs += float((rows + 1).sum())
-            elif kv_valid is not None:
-                pairs += float((kv_valid[rows] > 0).sum()) * float(kv_valid.sum())
-            else:
-                pairs += float(len(rows)) * n
-        rows_done += len(rows)
-    tflops = 4.0 * cfg.d * pairs / t_att / 1e12
-    return {"value": tflops, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
-            "sample": "oracle recipe attention on %d query rows of one head (%.1f s; quantisation "
-                      "of that head's Q/K/V took %.1f s, not in the value)" % (rows_done, t_att, t_quant)}
+            pairs += float(len(sel)) * float(keys)
+    else:
+        rows = np.sort(np.asarray(tokens, np.int64))
+        OA.recipe_attention(qo, ko, vo, rows, sm_scale=sm, bn=bn, causal=cfg.mode == "causal")
+        pairs = float((rows + 1).sum()) if cfg.mode == "causal" else float(len(rows)) * cfg.n_real
+    return pairs, time.perf_counter() - t0
+
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def cpu_baseline(cfg, x, bn, rows=4096):
+    """The oracle (as it stands) on the host cores: its quantisers on the full
+    Q, K, V tensors, then the recipe on `rows` seeded (head, query) rows drawn
+    uniformly over heads x real tokens; one worker process per core, heads
+    dealt over them, one BLAS thread each.  The value is the attention's
+    effective TFLOPS on the sampled rows (the same FLOP formula as the GPU:
+    4 d per computed pair); the quantisers' wall time is reported beside it."""
+    import multiprocessing as mp
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    heads, tokens = sample_rows(cfg, rows)
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores, initializer=_one_blas_thread) as pool:
+        t0 = time.perf_counter()
+        qjobs = [(cfg.name, x["q"][0, h], x["k"][0, h], x["v"][0, h]) for h in range(cfg.H)]
+        quant = pool.map(_oracle_quantize_head, qjobs, chunksize=1)
+        t_quant = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        ajobs = [(cfg.name, quant[h][0], tokens[heads == h], bn) for h in range(cfg.H)
+                 if np.any(heads == h)]
+        res = pool.map(_oracle_rows, ajobs, chunksize=1)
+        t_att = time.perf_counter() - t1
+    pairs = sum(p for p, _ in res)
+    in_bytes = 3 * x["q"].size * (2 if cfg.dtype == "bf16" else 4)
+    return {"value": 4.0 * cfg.d * pairs / t_att / 1e12, "unit": "TFLOPS", "cores": cores,
+            "kind": "oracle",
+            "sample": "oracle quantisers on the full Q, K, V (%d heads) in %.1f s (%.2f GB/s of "
+                      "input); oracle recipe attention on %d seeded (head, query) rows in %.1f s; "
+                      "%d worker processes" % (cfg.H, t_quant, in_bytes / t_quant / 1e9,
+                                               len(tokens), t_att, cores),
+            "quantize_s": round(t_quant, 3), "attention_s": round(t_att, 3), "rows": int(len(tokens)),
+            "attention_s_full_problem_extrapolated": round(
+                t_att / len(tokens) * cfg.H * cfg.n_real, 1)}
 
 
 def main():
@@ -401,7 +444,7 @@ def main():
         copy_calibration(args.copy_bytes)
     if not args.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, x, path.plan and _oracle_plan(cfg), bn)
+        result["cpu_baseline"] = cpu_baseline(cfg, x, bn)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))

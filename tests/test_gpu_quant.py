@@ -123,11 +123,11 @@ def test_mxfp4_bit_exact(gpu_lib, dtype):
     assert np.array_equal(OF.e2m1_unpack(qt.codes.cpu().numpy())[..., :300, :], codes)
 
 
-def _exhaustive_chunk(lo_bits, hi_bits):
-    """Every float32 bit pattern in [lo_bits, hi_bits) laid out as blocks of
-    16 tokens x 128 channels whose first element is 448, so each block's scale
-    is exactly 1 and the codes are the plain E4M3 conversion."""
-    pats = np.arange(lo_bits, hi_bits, dtype=np.uint32).view(np.float32)
+def _exhaustive_chunk(lo_bits, hi_bits, step=1):
+    """Every `step`-th float32 bit pattern in [lo_bits, hi_bits) laid out as
+    blocks of 16 tokens x 128 channels whose first element is 448, so each
+    block's scale is exactly 1 and the codes are the plain E4M3 conversion."""
+    pats = np.arange(lo_bits, hi_bits, step, dtype=np.uint32).view(np.float32)
     per = 16 * 128 - 1
     nblk = -(-len(pats) // per)
     buf = np.zeros(nblk * per, np.float32)
@@ -137,14 +137,20 @@ def _exhaustive_chunk(lo_bits, hi_bits):
     return blocks.reshape(1, 1, nblk * 16, 128), len(pats)
 
 
-@pytest.mark.parametrize("lo,hi", [(2.0 ** -12, 2.0 ** -4), (2.0 ** -4, 2.0 ** 2), (2.0 ** 2, 448.0)])
-def test_fp8_conversion_exhaustive_binades(gpu_lib, lo, hi):
+@pytest.mark.parametrize("lo,hi,step", [
+    (0.0, 2.0 ** -16, 251),           # +-0, float32 subnormals and tiny normals, sampled
+    (2.0 ** -16, 2.0 ** -12, 1),      # below the E4M3 grid: round to +-0 (0x80 for negatives)
+    (2.0 ** -12, 2.0 ** -4, 1), (2.0 ** -4, 2.0 ** 2, 1), (2.0 ** 2, 448.0, 1)])
+def test_fp8_conversion_exhaustive_binades(gpu_lib, lo, hi, step):
     """Device conversion against the oracle encoder for every float32 in [lo, hi)
-    and its negative."""
+    (every `step`-th bit pattern) and its negative; the negatives of values that
+    round to zero must give the code of -0 (0x80)."""
     lo_b = int(np.float32(lo).view(np.uint32))
     hi_b = int(np.float32(hi).view(np.uint32))
     for sign in (1.0, -1.0):
-        x, n = _exhaustive_chunk(lo_b, hi_b)
+        x, n = _exhaustive_chunk(lo_b, hi_b, step)
+        if sign < 0 and lo == 0.0:
+            assert np.signbit(np.float32(sign) * x.reshape(-1)[1])      # -0.0 is among the inputs
         x *= np.float32(sign)
         x[..., ::16, 0] = 448.0
         print("exhaustive", lo, hi, sign, n, flush=True)
