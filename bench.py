@@ -1,6 +1,7 @@
 """Benchmark of the block-scaled attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+    python bench.py --trace-summary DIR --steps K --warmup W
 
 One step is one pass of the whole path over one batch of synthetic input
 already resident in HBM: quantise Q, K, V (FP8 per block or MXFP4 for Q/K, FP8
@@ -365,6 +366,46 @@ def cpu_baseline(cfg, x, bn, rows=4096):
                 t_att / len(tokens) * cfg.H * cfg.n_real, 1)}
 
 
+def trace_summary(path, steps, warmup):
+    """Markdown summary of a rocprofv3 --kernel-trace CSV run of this script
+    (with the same --steps and --warmup): per kernel, the launches of the
+    timed steps only, the first `warmup` steps' launches left out.  A kernel
+    whose launch count is not a multiple of the step count (the counter
+    calibration copy) is listed with all its launches."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise SystemExit("no *kernel_trace.csv under %s" % path)
+    launches = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+                launches.setdefault(r["Kernel_Name"], []).append((t0, (t1 - t0) / 1e3))
+    total_steps = steps + warmup
+    rows, timed_total = [], 0.0
+    for name, lst in launches.items():
+        lst.sort()
+        per_step = len(lst) // total_steps
+        if per_step >= 1 and per_step * total_steps == len(lst):
+            durs = [d for _, d in lst[per_step * warmup:]]
+            note = "%d per step" % per_step
+        else:
+            durs = [d for _, d in lst]
+            note = "not per step: all launches"
+        timed_total += sum(durs)
+        rows.append((name.split("(")[0].replace("void ", ""), durs, note))
+    rows.sort(key=lambda r: -sum(r[1]))
+    out = ["| kernel | launches counted | median µs | mean µs | min µs | max µs | share of counted GPU time |",
+           "|---|---|---|---|---|---|---|"]
+    for name, durs, note in rows:
+        out.append("| `%s` | %d (%s) | %.1f | %.1f | %.1f | %.1f | %.2f%% |" % (
+            name, len(durs), note, float(np.median(durs)), float(np.mean(durs)), min(durs), max(durs),
+            100.0 * sum(durs) / timed_total))
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,7 +422,14 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device copy of this many bytes "
                          "(counter calibration for rocprofv3 --pmc runs)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print the per-kernel summary of a rocprofv3 --kernel-trace CSV run of this "
+                         "script made with the same --steps and --warmup (warm-up launches left out) "
+                         "and exit; needs no GPU")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.steps, args.warmup))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
