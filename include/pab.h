@@ -391,8 +391,11 @@ pab_status pab_attention_sta_backward(const pab_qview* q, const pab_qview* k, co
  *   kv_valid   uint8 [n_tokens]: 1 where perm >= 0;
  *   win_off    int32 [n_tiles+1], win_idx int32 [n_pairs]: window lists,
  *              ascending within each tile;
- *   lpt_order  int32 [n_tiles]: tiles by decreasing window size, ties by
- *              index.
+ *   lpt_order  int32 [n_tiles]: an issue order (results do not depend on
+ *              it): tiles by decreasing window size [FA4, LPT scheduling],
+ *              tiles with the same window list next to each other (ordered
+ *              by the list, then by index) so that their workgroups run
+ *              together and share the key tiles they read.
  * Pure host code, deterministic.
  */
 pab_status pab_sta_plan(const int grid[3], const int real_grid[3], const int tile[3],

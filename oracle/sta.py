@@ -32,7 +32,9 @@ def plan(grid, real_grid, tile, window):
        kv_valid  uint8 [N]: 1 where perm >= 0;
        win_off   int32 [M+1], win_idx int32 [sum |W|]: CSR window lists,
                  ascending tile index per row;
-       lpt       int32 [M]: tiles by decreasing |W(u)| (ties: lower index first);
+       lpt       int32 [M]: a schedule (no arithmetic depends on it): tiles by
+                 decreasing |W(u)|, then by their window list (so that tiles
+                 with the same list are adjacent), then by index;
        n_tokens, n_tiles, tile_tokens."""
     T, H, W = grid
     Tr, Hr, Wr = real_grid
@@ -59,7 +61,8 @@ def plan(grid, real_grid, tile, window):
         off.append(len(idx))
     off = np.array(off, dtype=np.int32)
     sizes = np.diff(off)
-    lpt = sorted(range(len(tiles)), key=lambda u: (-sizes[u], u))
+    lists = [tuple(idx[off[u]:off[u + 1]]) for u in range(len(tiles))]
+    lpt = sorted(range(len(tiles)), key=lambda u: (-sizes[u], lists[u], u))
     p = Plan()
     p.perm = perm
     p.kv_valid = (perm >= 0).astype(np.uint8)

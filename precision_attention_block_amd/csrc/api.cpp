@@ -681,10 +681,30 @@ pab_status pab_sta_plan(const int grid[3], const int real_grid[3], const int til
           if (win_off) win_off[u + 1] = (int32_t)pos;
         }
     if (lpt_order) {
+      // longest window lists first; among equal sizes, tiles with the same
+      // window list next to each other (ordered by the list, then by index),
+      // so that their workgroups run together and read the same key tiles
+      // in the same order, sharing the L2
+      std::vector<std::vector<int32_t>> lists(tiles);
+      int64_t v = 0;
+      for (int ut = 0; ut < nt[0]; ++ut)
+        for (int uh = 0; uh < nt[1]; ++uh)
+          for (int uw = 0; uw < nt[2]; ++uw, ++v) {
+            const int t0 = std::max(ut - rad[0], 0), t1 = std::min(ut + rad[0], nt[0] - 1);
+            const int h0 = std::max(uh - rad[1], 0), h1 = std::min(uh + rad[1], nt[1] - 1);
+            const int w0 = std::max(uw - rad[2], 0), w1 = std::min(uw + rad[2], nt[2] - 1);
+            for (int vt = t0; vt <= t1; ++vt)
+              for (int vh = h0; vh <= h1; ++vh)
+                for (int vw = w0; vw <= w1; ++vw)
+                  lists[v].push_back((int32_t)(((int64_t)vt * nt[1] + vh) * nt[2] + vw));
+          }
       std::vector<int32_t> order(tiles);
       std::iota(order.begin(), order.end(), 0);
-      std::stable_sort(order.begin(), order.end(),
-                       [&](int32_t x, int32_t y) { return sizes[x] > sizes[y]; });
+      std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+        if (sizes[x] != sizes[y]) return sizes[x] > sizes[y];
+        return std::lexicographical_compare(lists[x].begin(), lists[x].end(), lists[y].begin(),
+                                            lists[y].end());
+      });
       std::copy(order.begin(), order.end(), lpt_order);
     }
   }

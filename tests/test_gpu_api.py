@@ -160,3 +160,25 @@ def test_fp8_forward_needs_no_q_operand(gpu_lib, d, causal):
     _, bn = gpu_lib.attention_info("fp8_block", d, 1 if causal else 0)
     ref = _oracle_dense(x, "fp8", 64, causal, 1 / np.sqrt(d), bn)
     assert_close(b.cpu().numpy(), ref, "no Q operand d=%d causal=%s" % (d, causal))
+
+
+@pytest.mark.parametrize("recipe", ["fp8", "mxfp4"])
+def test_sta_result_does_not_depend_on_the_tile_order(gpu_lib, recipe):
+    """The plan's tile order only decides when each query tile's workgroups
+    run: issuing the tiles in reverse or in index order gives the same output
+    and row statistic, bit for bit."""
+    from precision_attention_block_amd import api
+    grid, real, tile, window = (4, 16, 24), (3, 15, 22), (2, 8, 8), (1, 3, 3)
+    hp = gpu_lib.sta_plan(grid, real, tile, window)
+    dp = gpu_lib.DevicePlan(hp, "cuda")
+    _, ts = _inputs(1, 2, int(np.prod(real)), 128, 93, torch.bfloat16, True)
+    qq, kq, vq = api.quantize_qkv(*(t.cuda() for t in ts), recipe, hp.tile_tokens, dp.perm, hp.n_tokens)
+    ref, ref_lse = gpu_lib.attention_sta(qq, kq, vq, dp, lse=True)
+    plan_order = dp.lpt.clone()
+    for order in (plan_order.flip(0), torch.arange(hp.n_tiles, dtype=torch.int32, device="cuda")):
+        dp.lpt = order.contiguous()
+        for steps in (False, True):
+            out, lse = gpu_lib.attention_sta(qq, kq, vq, dp, lse=True, steps=steps)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+    dp.lpt = plan_order
