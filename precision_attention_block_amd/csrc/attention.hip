@@ -40,7 +40,9 @@
 //  * one wave keeps both units busy: the softmax of tile t is interleaved
 //    with the P.V MFMAs of tile t-1 and the QK^T MFMAs of tile t+1.
 //  * workgroups are dealt to XCDs so that all query tiles of a head share an
-//    L2; causal query tiles are issued longest-first (LPT).
+//    L2; a causal workgroup computes a long and a short query tile of its
+//    head in turn (tiles n - 1 - p and p), so all causal workgroups carry the
+//    same work and the launch has no tail of short tiles.
 #include "pab_device.h"
 #include "pab_internal.h"
 #include "pab_lds.h"
@@ -238,11 +240,20 @@ __global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
   const int lr = lane & 31, lg = lane >> 5;     // MFMA column (query) and k-group
   const int work = xcd_work_index(blockIdx.x, gridDim.x);
 
-  int bh, q0, n_steps, u = 0;
+  int bh, q0 = 0, n_steps = 0, u = 0;
+  // causal: workgroup p of a head computes query tile n - 1 - p and then query
+  // tile p, so that every workgroup visits the same number of key tiles (n + 1
+  // steps of pairs of tiles) and the launch has no short tail
+  int pair = 0, n_pass = 1;
   // steps per window-list entry: an entry is a whole key tile (key_unit =
   // tile_tokens) or one BN-key step (key_unit = BN)
   const int spt = MODE == 2 ? a.key_unit / kBN : 1;
-  if (MODE == 2) {
+  if (MODE == 1) {
+    const int n_pairs = (a.n_qtiles + 1) / 2;
+    bh = work / n_pairs;
+    pair = work % n_pairs;
+    n_pass = pair < a.n_qtiles - 1 - pair ? 2 : 1;
+  } else if (MODE == 2) {
     const int sub = a.tile_tokens / kBM;               // query tiles per window tile
     const int per_bh = a.n_tiles * sub;
     bh = work / per_bh;
@@ -252,11 +263,8 @@ __global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
     n_steps = (a.win_off[u + 1] - a.win_off[u]) * spt;
   } else {
     bh = work / a.n_qtiles;
-    int qt = work % a.n_qtiles;
-    if (MODE == 1) qt = a.n_qtiles - 1 - qt;   // longest query tiles first
-    q0 = qt * kBM;
-    const int all = (a.N + kBN - 1) / kBN;
-    n_steps = MODE == 1 ? min((q0 + kBM) / kBN, all) : MODE == 3 ? a.n_key_tiles : all;
+    q0 = (work % a.n_qtiles) * kBM;
+    n_steps = MODE == 3 ? a.n_key_tiles : (a.N + kBN - 1) / kBN;
   }
   // Padding queries are stored nowhere: a workgroup made only of them (and
   // asked for no row statistic) has nothing to do.  Every wave checks all
@@ -266,554 +274,563 @@ __global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
                       (q0 + 64 + lane < a.N && a.out_perm[q0 + 64 + lane] >= 0);
     if (!__any(mine)) return;
   }
-  const int wq0 = q0 + wave * 32;             // first query of this wave
-  const int myq = wq0 + lr;                   // this lane's query
-  // The window list does not change during the launch: read through the
-  // constant address space its entries become scalar loads, whose completion
-  // counter is not the one the tile copies count on (a vector load would make
-  // every step wait for the copies issued before it).
-  typedef const __attribute__((address_space(4))) int32_t const_i32;
-  const_i32* wlist = MODE == 2 ? (const_i32*)(a.win_idx + a.win_off[u])
-                     : MODE == 3 ? (const_i32*)a.key_tiles : nullptr;
-  auto step_start = [&](int t) -> int {
-    if (MODE == 2) return wlist[t / spt] * a.key_unit + (t % spt) * kBN;
-    if (MODE == 3) return wlist[t] * kBN;
-    return t * kBN;
-  };
-
-  const int64_t tok0 = (int64_t)bh * a.n_alloc;
-  const uint8_t* kbh = (MX ? a.k : a.k16) + tok0 * TL::KROW;
-  const uint8_t* vbh = a.vt + (int64_t)bh * D * (V4 ? a.n_alloc / 2 : a.n_alloc);
-
-  // ---- Q operand (B of S^T = K Q^T), kept in registers for the whole pass.
-  // FP8: at MFMA step i lane (query lr, group lg) holds the 8 channels of
-  // chunk QI * lg + i; K is read with the same chunk order, so every channel
-  // pairs exactly once.  MXFP4: at step i the 32 channels of group 2 i + lg.
-  v8s qop16[QI];
-  v8i qop8[2];
-  int qsc[2] = {127, 127};
-  float cq;
-  {
-    const int64_t qrow = tok0 + myq;
-    if (MX) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        // E2M1 operands occupy the lower four registers; the upper four are
-        // never read and stay unset
-        v8i r;
-        const uint4 x = *reinterpret_cast<const uint4*>(a.q + qrow * (D / 2) + 16 * (2 * i + lg));
-        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
-        qop8[i] = r;
-        qsc[i] = a.q_mx[qrow * (D / 32) + 2 * i + lg];
-      }
-      cq = a.sm_log2;
-    } else {
-      load_q_codes<QI>(a.q + qrow * D + 8 * QI * lg, qop16);
-      cq = a.sm_log2 / a.q_scale[(int64_t)bh * a.nblk_q + myq / a.blk_q];
+  for (int pass = 0; pass < n_pass; ++pass) {
+    if (MODE == 1) {
+      q0 = (pass == 0 ? a.n_qtiles - 1 - pair : pair) * kBM;
+      n_steps = min((q0 + kBM) / kBN, (a.N + kBN - 1) / kBN);
     }
-  }
+    const int wq0 = q0 + wave * 32;             // first query of this wave
+    const int myq = wq0 + lr;                   // this lane's query
+    // The window list does not change during the launch: read through the
+    // constant address space its entries become scalar loads, whose completion
+    // counter is not the one the tile copies count on (a vector load would make
+    // every step wait for the copies issued before it).
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    const_i32* wlist = MODE == 2 ? (const_i32*)(a.win_idx + a.win_off[u])
+                       : MODE == 3 ? (const_i32*)a.key_tiles : nullptr;
+    auto step_start = [&](int t) -> int {
+      if (MODE == 2) return wlist[t / spt] * a.key_unit + (t % spt) * kBN;
+      if (MODE == 3) return wlist[t] * kBN;
+      return t * kBN;
+    };
 
-  float m_run = kNegInf, l_run = 0.0f;
-  v16f o[DB];
-#pragma unroll
-  for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) o[cb][j] = 0.0f;
+    const int64_t tok0 = (int64_t)bh * a.n_alloc;
+    const uint8_t* kbh = (MX ? a.k : a.k16) + tok0 * TL::KROW;
+    const uint8_t* vbh = a.vt + (int64_t)bh * D * (V4 ? a.n_alloc / 2 : a.n_alloc);
 
-  DmaPlan<TL::K_CPR> kp;
-  DmaPlan<TL::V_CPR> vp;
-  kp.init(lane, TL::KROW);
-  vp.init(lane, V4 ? a.n_alloc / 2 : a.n_alloc);
-  HeadBuffers hb;
-  hb.k = __builtin_amdgcn_make_buffer_rsrc((void*)kbh, 0, a.n_alloc * TL::KROW, kRsrcWord3);
-  hb.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbh, 0, (V4 ? a.n_alloc / 2 : a.n_alloc) * D,
-                                           kRsrcWord3);
-  hb.vs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(V4 ? a.v_mx + (int64_t)bh * (a.n_alloc / 32) * D : kbh), 0,
-      V4 ? (a.n_alloc / 32) * D : 0, kRsrcWord3);
-  hb.s = __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? a.k_mx + tok0 * (D / 32) : kbh), 0,
-                                           MX ? a.n_alloc * (D / 32) : 0, kRsrcWord3);
-  hb.has_mask = a.kv_valid != nullptr;
-  hb.m = __builtin_amdgcn_make_buffer_rsrc((void*)(hb.has_mask ? a.kv_valid : kbh), 0,
-                                           hb.has_mask ? a.N : 0, kRsrcWord3);
-  hb.blk_k = MX ? 1 : a.blk_k;
-  hb.c = __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? kbh : (const void*)(a.k_scale + (int64_t)bh * a.nblk_k)),
-                                           0, MX ? 0 : a.nblk_k * 4, kRsrcWord3);
-
-  // Per-lane byte offsets of this lane's operand chunks inside a stage; the
-  // rows are 32 kb + lr, so the swizzle depends on lr only (32, the rows per
-  // block, is a multiple of every swizzle period).
-  int k_off[MX ? 2 : QI];
-  if (MX) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) k_off[i] = lr * TL::KROW + 16 * ((2 * i + lg) ^ swz<4>(lr));
-  } else {
-#pragma unroll
-    for (int i = 0; i < QI; ++i) k_off[i] = lr * TL::KROW + 16 * ((QI * lg + i) ^ swz<TL::K_CPR>(lr));
-  }
-  const int v_off0 = lr * kBN + 16 * ((2 * lg) ^ swz<4>(lr));
-  const int v_off1 = lr * kBN + 16 * ((2 * lg + 1) ^ swz<4>(lr));
-  // FP4 P.V: the lane's 16-byte chunk (32 keys of group lg) of V^T row lr of
-  // a 32-channel block, and its dword of four E8M0 V scales (byte cb is the
-  // scale of channel 32 cb + lr and key group lg)
-  const int v_off4 = lr * TL::VROW + 16 * (lg ^ swz<2>(lr));
-  const int vsc_off = TL::VCODES + 128 * lg + 4 * lr;
-
-  // V^T operand of channel block cb from a V stage (FP4: only the lower four
-  // registers are set; the product below reads no more)
-  auto v_operand = [&](const uint8_t* Vs, const int cb) __attribute__((always_inline)) {
-    if (V4) {
-      const uint4 x = *reinterpret_cast<const uint4*>(Vs + cb * 32 * TL::VROW + v_off4);
-      v8i r;
-      r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
-      return r;
-    }
-    return make_v8(*reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off0),
-                   *reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off1));
-  };
-  // O^T[cb] += V^T P~^T: FP8 x FP8 with unit scales, or (FP4 P.V) E2M1 x E2M1
-  // with the V scale byte cb of vsc and the P scale ps of the lane's key group
-  auto pv_mfma = [&](const int cb, const v8i& vr, const v8i& pk, const uint32_t vsc, const int ps)
-      __attribute__((always_inline)) {
-    if (!V4) {
-      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vr, pk, o[cb], 0, 0, 0, 127, 0, 127);
-      return;
-    }
-    // E2M1 operands occupy four registers; the zero upper halves are never read
-    v8i a4 = {0, 0, 0, 0, 0, 0, 0, 0}, b4 = {0, 0, 0, 0, 0, 0, 0, 0};
-    a4[0] = vr[0]; a4[1] = vr[1]; a4[2] = vr[2]; a4[3] = vr[3];
-    b4[0] = pk[0]; b4[1] = pk[1]; b4[2] = pk[2]; b4[3] = pk[3];
-    if (cb == 0)
-      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 0, vsc, 0, ps);
-    else if (cb == 1)
-      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 1, vsc, 0, ps);
-    else if (cb == 2)
-      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 2, vsc, 0, ps);
-    else
-      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 3, vsc, 0, ps);
-  };
-
-  // S^T (keys x queries) of the key tile in K stage `Ks`, fp32 accumulate:
-  // s[kb][j] is key 32 kb + 8 (j / 4) + 4 lg + j % 4 of the tile, query myq.
-  auto qk = [&](const uint8_t* Ks, v16f (&s)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      v16f acc;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+    // ---- Q operand (B of S^T = K Q^T), kept in registers for the whole pass.
+    // FP8: at MFMA step i lane (query lr, group lg) holds the 8 channels of
+    // chunk QI * lg + i; K is read with the same chunk order, so every channel
+    // pairs exactly once.  MXFP4: at step i the 32 channels of group 2 i + lg.
+    v8s qop16[QI];
+    v8i qop8[2];
+    int qsc[2] = {127, 127};
+    float cq;
+    {
+      const int64_t qrow = tok0 + myq;
       if (MX) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          v8i kr;   // E2M1: only the lower four registers are read
-          const uint4 x = *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]);
-          kr[0] = x.x; kr[1] = x.y; kr[2] = x.z; kr[3] = x.w;
-          const int ksc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], acc, 4, 4, 0, ksc, 0,
-                                                                qsc[i]);
+          // E2M1 operands occupy the lower four registers; the upper four are
+          // never read and stay unset
+          v8i r;
+          const uint4 x = *reinterpret_cast<const uint4*>(a.q + qrow * (D / 2) + 16 * (2 * i + lg));
+          r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+          qop8[i] = r;
+          qsc[i] = a.q_mx[qrow * (D / 32) + 2 * i + lg];
         }
+        cq = a.sm_log2;
       } else {
-#pragma unroll
-        for (int i = 0; i < QI; ++i) {
-          const v8s kr = __builtin_bit_cast(
-              v8s, *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qop16[i], acc, 0, 0, 0);
-        }
-      }
-      s[kb] = acc;
-    }
-  };
-
-  // O^T += V^T P~^T for the tile in V stage `Vs`
-  auto pv = [&](const uint8_t* Vs, const v8i& pk, const int ps) __attribute__((always_inline)) {
-    const uint32_t vsc = V4 ? *reinterpret_cast<const uint32_t*>(Vs + vsc_off) : 0u;
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb) pv_mfma(cb, v_operand(Vs, cb), pk, vsc, ps);
-  };
-
-  // The MFMAs of one pipeline iteration, in issue order: m < DB is the P.V
-  // product of channel block m; m >= DB is step m - DB of S = K Q^T (key
-  // block kb = (m - DB) / QPB, step i = (m - DB) % QPB).
-  constexpr int QPB = MX ? 2 : QI;
-  constexpr int NM = DB + 2 * QPB;
-  constexpr int LA = MX ? 2 : 1;        // operand read lookahead, in slots
-  struct Op { v8i a; int sc; };
-  auto slot_lo = [](int g) constexpr { return g >= 8 ? NM : NM * g / 8; };
-  auto read_op = [&](const int m, const uint8_t* Vs, const uint8_t* Ks, Op& op)
-      __attribute__((always_inline)) {
-    if (m < DB) {
-      op.a = v_operand(Vs, m);
-    } else {
-      const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
-      const uint4 x = *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]);
-      op.a[0] = x.x; op.a[1] = x.y; op.a[2] = x.z; op.a[3] = x.w;
-      if (MX) op.sc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
-    }
-  };
-  auto issue_op = [&](const int m, const Op& op, v16f& acc0, v16f& acc1, const v8i& pk_in,
-                      const uint32_t vsc, const int ps_in) __attribute__((always_inline)) {
-    if (m < DB) {
-      pv_mfma(m, op.a, pk_in, vsc, ps_in);
-    } else {
-      const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
-      v16f c0;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) c0[j] = 0.0f;
-      if (MX) {
-        v8i kr;   // E2M1: only the lower four registers are read
-        kr[0] = op.a[0]; kr[1] = op.a[1]; kr[2] = op.a[2]; kr[3] = op.a[3];
-        v16f& acc = kb == 0 ? acc0 : acc1;
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], i == 0 ? c0 : acc,
-                                                                  4, 4, 0, op.sc, 0, qsc[i]);
-      } else {
-        v8s kr;
-        const v4i x = {op.a[0], op.a[1], op.a[2], op.a[3]};
-        kr = __builtin_bit_cast(v8s, x);
-        v16f& acc = kb == 0 ? acc0 : acc1;
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qop16[i], i == 0 ? c0 : acc, 0, 0, 0);
+        load_q_codes<QI>(a.q + qrow * D + 8 * QI * lg, qop16);
+        cq = a.sm_log2 / a.q_scale[(int64_t)bh * a.nblk_q + myq / a.blk_q];
       }
     }
-  };
 
-  // ---- prologue.  V stage v2 stands for tile -1: zero codes, so the first
-  // iteration's product with the zero P adds nothing.
-  // Copies run up to three tiles past the last one.  Dense and causal tiles
-  // past the end read zeros or in-bounds bytes of the same head (buffer
-  // loads check their range) into stages that are never read; list-driven
-  // steps (sliding-tile windows, listed key tiles) repeat the last listed
-  // tile, since the list ends there.
-  auto tile_at = [&](int t) { return MODE >= 2 ? step_start(min(t, n_steps - 1)) : t * kBN; };
-  issue_k<D, MX>(k0, hb, tile_at(0), wave, lane, kp);
-  issue_aux<D, MX>(x0, hb, tile_at(0), lane);
-  issue_k<D, MX>(k1, hb, tile_at(1), wave, lane, kp);
-  issue_aux<D, MX>(x1, hb, tile_at(1), lane);
-  issue_v<D, MX, V4>(v0, hb, a.n_alloc, tile_at(0), wave, lane, vp);
-  issue_k<D, MX>(k2, hb, tile_at(2), wave, lane, kp);
+    float m_run = kNegInf, l_run = 0.0f;
+    v16f o[DB];
 #pragma unroll
-  for (int i = tid * 16; i < TL::VBUF; i += 256 * 16)
-    *reinterpret_cast<uint4*>(v2 + i) = make_uint4(0u, 0u, 0u, 0u);
-  wait_vm_le<NV + NK>();          // V(0) and K(2) may still be in flight
-  barrier_lds();
+    for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[cb][j] = 0.0f;
 
-  // Score tiles: S(t) = (c0, c1) and S(t+1) = (n0, n1).  MXFP4 forms the
-  // next tile's key block 0 in slots 4-5, after this tile's block 0 has been
-  // read (slots 0-3), so the two share registers (ga): three tiles rotate
-  // instead of four, which saves 16 registers.  FP8 starts block 0 in slot 1.
-  v16f ga[2], gb[2], gc;
-  qk(k0, ga);
-  // P~ of the previous tile (read by the P.V MFMAs) and of the current one
-  // alternate between pa and pb like the score buffers
-  v8i pa = {0, 0, 0, 0, 0, 0, 0, 0}, pb = {0, 0, 0, 0, 0, 0, 0, 0};
-  int psa = 127, psb = 127;       // FP4 P.V: E8M0 scale of pa / pb for this lane's key group
-  barrier_lds();                  // every wave is done with k0 before K(3) is copied there
-  float alpha_prev = 1.0f;
+    DmaPlan<TL::K_CPR> kp;
+    DmaPlan<TL::V_CPR> vp;
+    kp.init(lane, TL::KROW);
+    vp.init(lane, V4 ? a.n_alloc / 2 : a.n_alloc);
+    HeadBuffers hb;
+    hb.k = __builtin_amdgcn_make_buffer_rsrc((void*)kbh, 0, a.n_alloc * TL::KROW, kRsrcWord3);
+    hb.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbh, 0, (V4 ? a.n_alloc / 2 : a.n_alloc) * D,
+                                             kRsrcWord3);
+    hb.vs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(V4 ? a.v_mx + (int64_t)bh * (a.n_alloc / 32) * D : kbh), 0,
+        V4 ? (a.n_alloc / 32) * D : 0, kRsrcWord3);
+    hb.s = __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? a.k_mx + tok0 * (D / 32) : kbh), 0,
+                                             MX ? a.n_alloc * (D / 32) : 0, kRsrcWord3);
+    hb.has_mask = a.kv_valid != nullptr;
+    hb.m = __builtin_amdgcn_make_buffer_rsrc((void*)(hb.has_mask ? a.kv_valid : kbh), 0,
+                                             hb.has_mask ? a.N : 0, kRsrcWord3);
+    hb.blk_k = MX ? 1 : a.blk_k;
+    hb.c = __builtin_amdgcn_make_buffer_rsrc((void*)(MX ? kbh : (const void*)(a.k_scale + (int64_t)bh * a.nblk_k)),
+                                             0, MX ? 0 : a.nblk_k * 4, kRsrcWord3);
 
-  // Iteration t: K stages Kr (t+1, read) and Kw (t+3, written); V stages Vr
-  // (t-1, read) and Vw (t+1, written); side stages Ar (t, read), Aw (t+2, written).
-  auto iter = [&](const int t, const uint8_t* Kr, uint8_t* Kw, const uint8_t* Vr, uint8_t* Vw,
-                  const uint8_t* Ar, uint8_t* Aw, v16f& c0s, v16f& c1s, v16f& n0s, v16f& n1s,
-                  const v8i& pk_in, v8i& pk, const int ps_in, int& ps_out)
-      __attribute__((always_inline)) {
-    auto s_cur = [&](int kb) __attribute__((always_inline)) -> v16f& { return kb == 0 ? c0s : c1s; };
-    const int ks = step_start(t);
-    // this iteration's copies (K(t+3), V(t+1), side data of t+2) are issued
-    // one instruction per slot below: issued back to back by every wave they
-    // would queue up at the texture unit and stall the issuing waves
-    const int ks_k = tile_at(t + 3), ks_v = tile_at(t + 1), ks_a = tile_at(t + 2);
-    auto copy_item = [&](const int j) __attribute__((always_inline)) {
-      constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI, KPER = DmaPlan<TL::K_CPR>::PER;
-      if (j < TL::KI) {
-        const int inst = wave * TL::KI + j;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(Kw + inst * 1024), 16,
-                                                 kp.off[inst % KPER], (ks_k + inst * KRPI) * TL::KROW, 0, 0);
-      } else if (MX && j == TL::KI) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(Kw + TL::K_BYTES), 4, 4 * lane,
-                                                 ks_k * (D / 32), 0, 0);
-      } else if (j < NK + TL::VI) {
-        issue_v_inst<D, MX, V4>(Vw, hb, a.n_alloc, ks_v, wave * TL::VI + (j - NK), vp);
-      } else if (V4 && j == NK + TL::VI) {
-        issue_vscale<D, MX, V4>(Vw, hb, ks_v, lane);
-      } else if (j == NK + NV) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.m, (lds_void_t*)Aw, 4, 4 * lane, ks_a, 0, 0);
-      } else if (!MX && j == NK + NV + 1) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.c, (lds_void_t*)(Aw + TL::M_BYTES), 4, 4 * lane,
-                                                 (ks_a / hb.blk_k) * 4, 0, 0);
-      }
-    };
-    static_assert(NK + NV + NA <= 8, "one copy instruction per slot");
-
-    // dequantisation factor c (log2 domain): c = sm_scale log2(e) / (s_Q s_K),
-    // per group of 4 keys (kb, j / 4); constant over the tile when UK.
-    const float* Cs = reinterpret_cast<const float*>(Ar + TL::M_BYTES);
-    float c[8];
+    // Per-lane byte offsets of this lane's operand chunks inside a stage; the
+    // rows are 32 kb + lr, so the swizzle depends on lr only (32, the rows per
+    // block, is a multiple of every swizzle period).
+    int k_off[MX ? 2 : QI];
     if (MX) {
 #pragma unroll
-      for (int g = 0; g < 8; ++g) c[g] = cq;
-    } else if (UK) {
-      const float ck = cq * __builtin_amdgcn_rcpf(Cs[0]);
-#pragma unroll
-      for (int g = 0; g < 8; ++g) c[g] = ck;
+      for (int i = 0; i < 2; ++i) k_off[i] = lr * TL::KROW + 16 * ((2 * i + lg) ^ swz<4>(lr));
     } else {
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {   // Cs[i] is the scale of block ks / blk + i
-        const int key = ks + 32 * (g / 4) + 8 * (g % 4);
-        c[g] = cq * __builtin_amdgcn_rcpf(Cs[key / a.blk_k - ks / a.blk_k]);
+      for (int i = 0; i < QI; ++i) k_off[i] = lr * TL::KROW + 16 * ((QI * lg + i) ^ swz<TL::K_CPR>(lr));
+    }
+    const int v_off0 = lr * kBN + 16 * ((2 * lg) ^ swz<4>(lr));
+    const int v_off1 = lr * kBN + 16 * ((2 * lg + 1) ^ swz<4>(lr));
+    // FP4 P.V: the lane's 16-byte chunk (32 keys of group lg) of V^T row lr of
+    // a 32-channel block, and its dword of four E8M0 V scales (byte cb is the
+    // scale of channel 32 cb + lr and key group lg)
+    const int v_off4 = lr * TL::VROW + 16 * (lg ^ swz<2>(lr));
+    const int vsc_off = TL::VCODES + 128 * lg + 4 * lr;
+
+    // V^T operand of channel block cb from a V stage (FP4: only the lower four
+    // registers are set; the product below reads no more)
+    auto v_operand = [&](const uint8_t* Vs, const int cb) __attribute__((always_inline)) {
+      if (V4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(Vs + cb * 32 * TL::VROW + v_off4);
+        v8i r;
+        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+        return r;
       }
-    }
-    // O = alpha(t-1) O: the product of tile t-2 (issued one iteration ago)
-    // has landed, that of tile t-1 is issued below; only when some row max
-    // moved
-    if (__builtin_amdgcn_ballot_w64(alpha_prev != 1.0f) != 0) {
+      return make_v8(*reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off0),
+                     *reinterpret_cast<const uint4*>(Vs + cb * 32 * kBN + v_off1));
+    };
+    // O^T[cb] += V^T P~^T: FP8 x FP8 with unit scales, or (FP4 P.V) E2M1 x E2M1
+    // with the V scale byte cb of vsc and the P scale ps of the lane's key group
+    auto pv_mfma = [&](const int cb, const v8i& vr, const v8i& pk, const uint32_t vsc, const int ps)
+        __attribute__((always_inline)) {
+      if (!V4) {
+        o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vr, pk, o[cb], 0, 0, 0, 127, 0, 127);
+        return;
+      }
+      // E2M1 operands occupy four registers; the zero upper halves are never read
+      v8i a4 = {0, 0, 0, 0, 0, 0, 0, 0}, b4 = {0, 0, 0, 0, 0, 0, 0, 0};
+      a4[0] = vr[0]; a4[1] = vr[1]; a4[2] = vr[2]; a4[3] = vr[3];
+      b4[0] = pk[0]; b4[1] = pk[1]; b4[2] = pk[2]; b4[3] = pk[3];
+      if (cb == 0)
+        o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 0, vsc, 0, ps);
+      else if (cb == 1)
+        o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 1, vsc, 0, ps);
+      else if (cb == 2)
+        o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 2, vsc, 0, ps);
+      else
+        o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, o[cb], 4, 4, 3, vsc, 0, ps);
+    };
+
+    // S^T (keys x queries) of the key tile in K stage `Ks`, fp32 accumulate:
+    // s[kb][j] is key 32 kb + 8 (j / 4) + 4 lg + j % 4 of the tile, query myq.
+    auto qk = [&](const uint8_t* Ks, v16f (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha_prev;
-    }
-    // masks: padding keys (staged with the tile), keys past N, the causal
-    // diagonal; the tests are wave-uniform, the masking branch-free
-    const bool edge = (ks + kBN > a.N) || (MODE == 1 && ks + kBN - 1 > wq0);
-    if (edge || hb.has_mask) {
-      const bool partial = hb.has_mask && Ar[lane] == 0;
-      if (edge || __builtin_amdgcn_ballot_w64(partial) != 0) {
-        const int lim = MODE == 1 ? min(a.N - 1, myq) : a.N - 1;   // last admissible key
+      for (int kb = 0; kb < 2; ++kb) {
+        v16f acc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+        if (MX) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            v8i kr;   // E2M1: only the lower four registers are read
+            const uint4 x = *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]);
+            kr[0] = x.x; kr[1] = x.y; kr[2] = x.z; kr[3] = x.w;
+            const int ksc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], acc, 4, 4, 0, ksc, 0,
+                                                                  qsc[i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < QI; ++i) {
+            const v8s kr = __builtin_bit_cast(
+                v8s, *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qop16[i], acc, 0, 0, 0);
+          }
+        }
+        s[kb] = acc;
+      }
+    };
+
+    // O^T += V^T P~^T for the tile in V stage `Vs`
+    auto pv = [&](const uint8_t* Vs, const v8i& pk, const int ps) __attribute__((always_inline)) {
+      const uint32_t vsc = V4 ? *reinterpret_cast<const uint32_t*>(Vs + vsc_off) : 0u;
+#pragma unroll
+      for (int cb = 0; cb < DB; ++cb) pv_mfma(cb, v_operand(Vs, cb), pk, vsc, ps);
+    };
+
+    // The MFMAs of one pipeline iteration, in issue order: m < DB is the P.V
+    // product of channel block m; m >= DB is step m - DB of S = K Q^T (key
+    // block kb = (m - DB) / QPB, step i = (m - DB) % QPB).
+    constexpr int QPB = MX ? 2 : QI;
+    constexpr int NM = DB + 2 * QPB;
+    constexpr int LA = MX ? 2 : 1;        // operand read lookahead, in slots
+    struct Op { v8i a; int sc; };
+    auto slot_lo = [](int g) constexpr { return g >= 8 ? NM : NM * g / 8; };
+    auto read_op = [&](const int m, const uint8_t* Vs, const uint8_t* Ks, Op& op)
+        __attribute__((always_inline)) {
+      if (m < DB) {
+        op.a = v_operand(Vs, m);
+      } else {
+        const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
+        const uint4 x = *reinterpret_cast<const uint4*>(Ks + kb * 32 * TL::KROW + k_off[i]);
+        op.a[0] = x.x; op.a[1] = x.y; op.a[2] = x.z; op.a[3] = x.w;
+        if (MX) op.sc = Ks[TL::K_BYTES + (32 * kb + lr) * (D / 32) + 2 * i + lg];
+      }
+    };
+    auto issue_op = [&](const int m, const Op& op, v16f& acc0, v16f& acc1, const v8i& pk_in,
+                        const uint32_t vsc, const int ps_in) __attribute__((always_inline)) {
+      if (m < DB) {
+        pv_mfma(m, op.a, pk_in, vsc, ps_in);
+      } else {
+        const int kb = (m - DB) / QPB, i = (m - DB) % QPB;
+        v16f c0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c0[j] = 0.0f;
+        if (MX) {
+          v8i kr;   // E2M1: only the lower four registers are read
+          kr[0] = op.a[0]; kr[1] = op.a[1]; kr[2] = op.a[2]; kr[3] = op.a[3];
+          v16f& acc = kb == 0 ? acc0 : acc1;
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kr, qop8[i], i == 0 ? c0 : acc,
+                                                                    4, 4, 0, op.sc, 0, qsc[i]);
+        } else {
+          v8s kr;
+          const v4i x = {op.a[0], op.a[1], op.a[2], op.a[3]};
+          kr = __builtin_bit_cast(v8s, x);
+          v16f& acc = kb == 0 ? acc0 : acc1;
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qop16[i], i == 0 ? c0 : acc, 0, 0, 0);
+        }
+      }
+    };
+
+    // ---- prologue.  V stage v2 stands for tile -1: zero codes, so the first
+    // iteration's product with the zero P adds nothing.
+    // Copies run up to three tiles past the last one.  Dense and causal tiles
+    // past the end read zeros or in-bounds bytes of the same head (buffer
+    // loads check their range) into stages that are never read; list-driven
+    // steps (sliding-tile windows, listed key tiles) repeat the last listed
+    // tile, since the list ends there.
+    auto tile_at = [&](int t) { return MODE >= 2 ? step_start(min(t, n_steps - 1)) : t * kBN; };
+    issue_k<D, MX>(k0, hb, tile_at(0), wave, lane, kp);
+    issue_aux<D, MX>(x0, hb, tile_at(0), lane);
+    issue_k<D, MX>(k1, hb, tile_at(1), wave, lane, kp);
+    issue_aux<D, MX>(x1, hb, tile_at(1), lane);
+    issue_v<D, MX, V4>(v0, hb, a.n_alloc, tile_at(0), wave, lane, vp);
+    issue_k<D, MX>(k2, hb, tile_at(2), wave, lane, kp);
+#pragma unroll
+    for (int i = tid * 16; i < TL::VBUF; i += 256 * 16)
+      *reinterpret_cast<uint4*>(v2 + i) = make_uint4(0u, 0u, 0u, 0u);
+    wait_vm_le<NV + NK>();          // V(0) and K(2) may still be in flight
+    barrier_lds();
+
+    // Score tiles: S(t) = (c0, c1) and S(t+1) = (n0, n1).  MXFP4 forms the
+    // next tile's key block 0 in slots 4-5, after this tile's block 0 has been
+    // read (slots 0-3), so the two share registers (ga): three tiles rotate
+    // instead of four, which saves 16 registers.  FP8 starts block 0 in slot 1.
+    v16f ga[2], gb[2], gc;
+    qk(k0, ga);
+    // P~ of the previous tile (read by the P.V MFMAs) and of the current one
+    // alternate between pa and pb like the score buffers
+    v8i pa = {0, 0, 0, 0, 0, 0, 0, 0}, pb = {0, 0, 0, 0, 0, 0, 0, 0};
+    int psa = 127, psb = 127;       // FP4 P.V: E8M0 scale of pa / pb for this lane's key group
+    barrier_lds();                  // every wave is done with k0 before K(3) is copied there
+    float alpha_prev = 1.0f;
+
+    // Iteration t: K stages Kr (t+1, read) and Kw (t+3, written); V stages Vr
+    // (t-1, read) and Vw (t+1, written); side stages Ar (t, read), Aw (t+2, written).
+    auto iter = [&](const int t, const uint8_t* Kr, uint8_t* Kw, const uint8_t* Vr, uint8_t* Vw,
+                    const uint8_t* Ar, uint8_t* Aw, v16f& c0s, v16f& c1s, v16f& n0s, v16f& n1s,
+                    const v8i& pk_in, v8i& pk, const int ps_in, int& ps_out)
+        __attribute__((always_inline)) {
+      auto s_cur = [&](int kb) __attribute__((always_inline)) -> v16f& { return kb == 0 ? c0s : c1s; };
+      const int ks = step_start(t);
+      // this iteration's copies (K(t+3), V(t+1), side data of t+2) are issued
+      // one instruction per slot below: issued back to back by every wave they
+      // would queue up at the texture unit and stall the issuing waves
+      const int ks_k = tile_at(t + 3), ks_v = tile_at(t + 1), ks_a = tile_at(t + 2);
+      auto copy_item = [&](const int j) __attribute__((always_inline)) {
+        constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI, KPER = DmaPlan<TL::K_CPR>::PER;
+        if (j < TL::KI) {
+          const int inst = wave * TL::KI + j;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(Kw + inst * 1024), 16,
+                                                   kp.off[inst % KPER], (ks_k + inst * KRPI) * TL::KROW, 0, 0);
+        } else if (MX && j == TL::KI) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(Kw + TL::K_BYTES), 4, 4 * lane,
+                                                   ks_k * (D / 32), 0, 0);
+        } else if (j < NK + TL::VI) {
+          issue_v_inst<D, MX, V4>(Vw, hb, a.n_alloc, ks_v, wave * TL::VI + (j - NK), vp);
+        } else if (V4 && j == NK + TL::VI) {
+          issue_vscale<D, MX, V4>(Vw, hb, ks_v, lane);
+        } else if (j == NK + NV) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.m, (lds_void_t*)Aw, 4, 4 * lane, ks_a, 0, 0);
+        } else if (!MX && j == NK + NV + 1) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.c, (lds_void_t*)(Aw + TL::M_BYTES), 4, 4 * lane,
+                                                   (ks_a / hb.blk_k) * 4, 0, 0);
+        }
+      };
+      static_assert(NK + NV + NA <= 8, "one copy instruction per slot");
+
+      // dequantisation factor c (log2 domain): c = sm_scale log2(e) / (s_Q s_K),
+      // per group of 4 keys (kb, j / 4); constant over the tile when UK.
+      const float* Cs = reinterpret_cast<const float*>(Ar + TL::M_BYTES);
+      float c[8];
+      if (MX) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) c[g] = cq;
+      } else if (UK) {
+        const float ck = cq * __builtin_amdgcn_rcpf(Cs[0]);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) c[g] = ck;
+      } else {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {   // Cs[i] is the scale of block ks / blk + i
+          const int key = ks + 32 * (g / 4) + 8 * (g % 4);
+          c[g] = cq * __builtin_amdgcn_rcpf(Cs[key / a.blk_k - ks / a.blk_k]);
+        }
+      }
+      // O = alpha(t-1) O: the product of tile t-2 (issued one iteration ago)
+      // has landed, that of tile t-1 is issued below; only when some row max
+      // moved
+      if (__builtin_amdgcn_ballot_w64(alpha_prev != 1.0f) != 0) {
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha_prev;
+      }
+      // masks: padding keys (staged with the tile), keys past N, the causal
+      // diagonal; the tests are wave-uniform, the masking branch-free
+      const bool edge = (ks + kBN > a.N) || (MODE == 1 && ks + kBN - 1 > wq0);
+      if (edge || hb.has_mask) {
+        const bool partial = hb.has_mask && Ar[lane] == 0;
+        if (edge || __builtin_amdgcn_ballot_w64(partial) != 0) {
+          const int lim = MODE == 1 ? min(a.N - 1, myq) : a.N - 1;   // last admissible key
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const uint32_t w = hb.has_mask
+                  ? *reinterpret_cast<const uint32_t*>(Ar + 32 * kb + 8 * g4 + 4 * lg) : 0x01010101u;
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                const int key = ks + 32 * kb + 8 * g4 + 4 * lg + jj;
+                const bool ok = (key <= lim) & (((w >> (8 * jj)) & 0xFFu) != 0u);
+                s_cur(kb)[4 * g4 + jj] = ok ? s_cur(kb)[4 * g4 + jj] : kNegInf;
+              }
+            }
+        }
+      }
+
+      // operands of the first LA slots (and the FP4 V scales of the tile)
+      Op ops[NM];
+#pragma unroll
+      for (int m = 0; m < slot_lo(LA); ++m) read_op(m, Vr, Kr, ops[m]);
+      const uint32_t vsc = V4 ? *reinterpret_cast<const uint32_t*>(Vr + vsc_off) : 0u;
+
+      // running max; with one factor c for the whole tile (c > 0) the max of
+      // c s is c times the max of s
+      float mx;
+      float gmax[2];   // FP4 P.V: maximum score of each 32-key group of the row
+      if (V4) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const v16f& x = s_cur(kb);
+          const float t0 = max3f(x[0], x[1], x[2]), t1 = max3f(x[3], x[4], x[5]);
+          const float t2 = max3f(x[6], x[7], x[8]), t3 = max3f(x[9], x[10], x[11]);
+          const float t4 = max3f(x[12], x[13], x[14]);
+          gmax[kb] = swap_max(max3f(max3f(t0, t1, t2), t3, fmaxf(t4, x[15])));
+        }
+        mx = c[0] * fmaxf(gmax[0], gmax[1]);
+      } else if (MX || UK) {
+        // max3 tree over the lane's 32 scores
+        float m11[11];
+#pragma unroll
+        for (int i = 0; i < 10; ++i) {
+          const int e = 3 * i;
+          m11[i] = max3f(s_cur(e / 16)[e % 16], s_cur((e + 1) / 16)[(e + 1) % 16],
+                         s_cur((e + 2) / 16)[(e + 2) % 16]);
+        }
+        m11[10] = fmaxf(s_cur(1)[14], s_cur(1)[15]);
+        const float m = max3f(max3f(m11[0], m11[1], m11[2]), max3f(m11[3], m11[4], m11[5]),
+                              max3f(max3f(m11[6], m11[7], m11[8]), m11[9], m11[10]));
+        mx = c[0] * m;
+      } else {
+        mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const uint32_t w = hb.has_mask
-                ? *reinterpret_cast<const uint32_t*>(Ar + 32 * kb + 8 * g4 + 4 * lg) : 0x01010101u;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int key = ks + 32 * kb + 8 * g4 + 4 * lg + jj;
-              const bool ok = (key <= lim) & (((w >> (8 * jj)) & 0xFFu) != 0u);
-              s_cur(kb)[4 * g4 + jj] = ok ? s_cur(kb)[4 * g4 + jj] : kNegInf;
-            }
+            const float m4 = fmaxf(fmaxf(s_cur(kb)[4 * g4], s_cur(kb)[4 * g4 + 1]),
+                                   fmaxf(s_cur(kb)[4 * g4 + 2], s_cur(kb)[4 * g4 + 3]));
+            mx = fmaxf(mx, c[4 * kb + g4] * m4);
           }
       }
-    }
-
-    // operands of the first LA slots (and the FP4 V scales of the tile)
-    Op ops[NM];
-#pragma unroll
-    for (int m = 0; m < slot_lo(LA); ++m) read_op(m, Vr, Kr, ops[m]);
-    const uint32_t vsc = V4 ? *reinterpret_cast<const uint32_t*>(Vr + vsc_off) : 0u;
-
-    // running max; with one factor c for the whole tile (c > 0) the max of
-    // c s is c times the max of s
-    float mx;
-    float gmax[2];   // FP4 P.V: maximum score of each 32-key group of the row
-    if (V4) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const v16f& x = s_cur(kb);
-        const float t0 = max3f(x[0], x[1], x[2]), t1 = max3f(x[3], x[4], x[5]);
-        const float t2 = max3f(x[6], x[7], x[8]), t3 = max3f(x[9], x[10], x[11]);
-        const float t4 = max3f(x[12], x[13], x[14]);
-        gmax[kb] = swap_max(max3f(max3f(t0, t1, t2), t3, fmaxf(t4, x[15])));
-      }
-      mx = c[0] * fmaxf(gmax[0], gmax[1]);
-    } else if (MX || UK) {
-      // max3 tree over the lane's 32 scores
-      float m11[11];
-#pragma unroll
-      for (int i = 0; i < 10; ++i) {
-        const int e = 3 * i;
-        m11[i] = max3f(s_cur(e / 16)[e % 16], s_cur((e + 1) / 16)[(e + 1) % 16],
-                       s_cur((e + 2) / 16)[(e + 2) % 16]);
-      }
-      m11[10] = fmaxf(s_cur(1)[14], s_cur(1)[15]);
-      const float m = max3f(max3f(m11[0], m11[1], m11[2]), max3f(m11[3], m11[4], m11[5]),
-                            max3f(max3f(m11[6], m11[7], m11[8]), m11[9], m11[10]));
-      mx = c[0] * m;
-    } else {
-      mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float m4 = fmaxf(fmaxf(s_cur(kb)[4 * g4], s_cur(kb)[4 * g4 + 1]),
-                                 fmaxf(s_cur(kb)[4 * g4 + 2], s_cur(kb)[4 * g4 + 3]));
-          mx = fmaxf(mx, c[4 * kb + g4] * m4);
-        }
-    }
-    if (!V4) mx = swap_max(mx);
-    // the reference maximum moves only when the row maximum exceeds it by
-    // more than tau (tau = 0: on every rise); P = 2^(S c - m) <= 2^tau is
-    // quantised with the scale 448 / 2^tau
-    const float cand = fmaxf(m_run, mx);
-    const float mnew = cand > m_run + a.tau ? cand : m_run;
-    const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
-    const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448 + a.tau;
-    m_run = mnew;
-    // FP4 P.V: the MX rule per key group, e = floor(log2 max P) - 2 read from
-    // the exponent of 2^(c gmax - m) (-127 for an empty or subnormal group);
-    // the exponentials below then give P / 2^e in [0, 8).  c gmax is rounded
-    // as a product of its own, exactly as the row maximum above, so that the
-    // group holding the maximum gets 2^0 = 1 (a fused multiply-add would
-    // leave the product's rounding error, and 2^-tiny sets e one too low);
-    // the empty asm keeps the compiler from fusing the two.
-    int eg[2] = {0, 0};
-    float mshg[2] = {msh, msh};
-    if (V4) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float cg = c[0] * gmax[kb];
-        asm volatile("" : "+v"(cg));
-        const float pmax = gmax[kb] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(cg - mnew);
-        const int eb = (int)(__float_as_uint(pmax) >> 23);
-        eg[kb] = eb == 0 ? -127 : max(eb - 129, -127);
-        mshg[kb] = mnew == kNegInf ? 0.0f : mnew + (float)eg[kb];
-      }
-    }
-
-    // The previous tile's P.V and the next tile's S are independent MFMAs;
-    // they are dealt over 8 slots, one per group of 4 exponentials, and each
-    // slot's operands are read from LDS LA slots ahead (a slot is shorter
-    // than an LDS read's latency).  The order is pinned
-    // with empty volatile asm statements (kept in program order): a slot's
-    // MFMAs take their operands from one, and its exponentials end in one.
-    float gs[8];
-    float pq[4];   // exponentials of the previous group, packed one slot later
-    uint32_t pk4[4];   // FP4 P.V: E2M1 codes, 8 per dword, dwords 0-1 key group 0
-    // packs group g's four P values (E4M3, or E2M1 for FP4 P.V) and sums them;
-    // runs one slot after their exponentials so that the exp latency is hidden
-    // by other work
-    auto finish = [&](const int g) __attribute__((always_inline)) {
-      gs[g] = (pq[0] + pq[1]) + (pq[2] + pq[3]);
+      if (!V4) mx = swap_max(mx);
+      // the reference maximum moves only when the row maximum exceeds it by
+      // more than tau (tau = 0: on every rise); P = 2^(S c - m) <= 2^tau is
+      // quantised with the scale 448 / 2^tau
+      const float cand = fmaxf(m_run, mx);
+      const float mnew = cand > m_run + a.tau ? cand : m_run;
+      const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
+      const float msh = mnew == kNegInf ? 0.0f : mnew - kLog2_448 + a.tau;
+      m_run = mnew;
+      // FP4 P.V: the MX rule per key group, e = floor(log2 max P) - 2 read from
+      // the exponent of 2^(c gmax - m) (-127 for an empty or subnormal group);
+      // the exponentials below then give P / 2^e in [0, 8).  c gmax is rounded
+      // as a product of its own, exactly as the row maximum above, so that the
+      // group holding the maximum gets 2^0 = 1 (a fused multiply-add would
+      // leave the product's rounding error, and 2^-tiny sets e one too low);
+      // the empty asm keeps the compiler from fusing the two.
+      int eg[2] = {0, 0};
+      float mshg[2] = {msh, msh};
       if (V4) {
-        uint32_t w;
-        if ((g & 1) == 0) {
-          asm volatile("" : "=v"(w));   // bytes 0-1 written here, 2-3 by group g + 1
-          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pq[0], pq[1], 1.0f, 0);
-          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pq[2], pq[3], 1.0f, 1);
-        } else {
-          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk4[g / 2], pq[0], pq[1], 1.0f, 2);
-          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pq[2], pq[3], 1.0f, 3);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float cg = c[0] * gmax[kb];
+          asm volatile("" : "+v"(cg));
+          const float pmax = gmax[kb] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(cg - mnew);
+          const int eb = (int)(__float_as_uint(pmax) >> 23);
+          eg[kb] = eb == 0 ? -127 : max(eb - 129, -127);
+          mshg[kb] = mnew == kNegInf ? 0.0f : mnew + (float)eg[kb];
         }
-        asm volatile("" : "+v"(w), "+v"(gs[g]));
-        pk4[g / 2] = w;
-        return;
       }
-      int w;
-      asm volatile("" : "=v"(w));   // the two conversions below write all four bytes
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], w, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], w, true);
-      asm volatile("" : "+v"(w), "+v"(gs[g]));
-      pk[g] = w;
-    };
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      copy_item(g);
-#pragma unroll
-      for (int m = slot_lo(g); m < slot_lo(g + 1); ++m) {
-        if (MX && !V4 && m >= DB) {
-          // an E2M1 K operand lives in its lower four registers
-          v4i lo = {ops[m].a[0], ops[m].a[1], ops[m].a[2], ops[m].a[3]};
-          asm volatile("" : "+v"(lo));
-          ops[m].a[0] = lo[0]; ops[m].a[1] = lo[1]; ops[m].a[2] = lo[2]; ops[m].a[3] = lo[3];
-        } else {
-          asm volatile("" : "+v"(ops[m].a));
-        }
-        issue_op(m, ops[m], n0s, n1s, pk_in, vsc, ps_in);
-      }
-#pragma unroll
-      for (int m = slot_lo(g + LA); m < slot_lo(g + LA + 1); ++m) read_op(m, Vr, Kr, ops[m]);
-      const int kb = g / 4, g4 = g % 4;
-      const float cc = c[g];
-      const float sh = V4 ? mshg[kb] : msh;
-      float pn[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pn[j] = __builtin_amdgcn_exp2f(fmaf(s_cur(kb)[4 * g4 + j], cc, -sh));
-      if (g > 0) finish(g - 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pq[j] = pn[j];
-    }
-    finish(7);
-    float sum;
-    if (V4) {
-      // B operand of the FP4 P.V product: lane half lg takes key group lg, its
-      // own 16 codes of that group and the other half's 16 (K slot order
-      // 8 b + r, then 8 b + 4 + r of the group, b, r < 4)
-      const auto t0 = __builtin_amdgcn_permlane32_swap(pk4[0], pk4[2], false, false);
-      const auto t1 = __builtin_amdgcn_permlane32_swap(pk4[1], pk4[3], false, false);
-      pk[0] = (int)t0[0]; pk[1] = (int)t1[0]; pk[2] = (int)t0[1]; pk[3] = (int)t1[1];
-      ps_out = 127 + (lg == 0 ? eg[0] : eg[1]);
-      sum = ldexpf((gs[0] + gs[1]) + (gs[2] + gs[3]), eg[0]) +
-            ldexpf((gs[4] + gs[5]) + (gs[6] + gs[7]), eg[1]);
-    } else {
-      sum = ((gs[0] + gs[1]) + (gs[2] + gs[3])) + ((gs[4] + gs[5]) + (gs[6] + gs[7]));
-    }
-    l_run = l_run * alpha + sum;
-    alpha_prev = alpha;
-    // K(t+2), V(t) and the side stage of t+1 must have landed; this
-    // iteration's copies may not have
-    wait_vm_le<NK + NV + NA>();
-    barrier_lds();
-  };
-  // unrolled by 6: the stage rings have period 3 and the two score buffers
-  // alternate, so no buffer is ever copied
-  for (int t = 0; t < n_steps; t += 6) {
-    // even t: S(t) in (ga0, ga1) -> S(t+1) in (MX ? ga0 : gb0, MX ? gc : gb1);
-    // odd t: S(t) in (MX ? ga0 : gb0, MX ? gc : gb1) -> S(t+1) in (ga0, ga1)
-    v16f& e0 = ga[0];
-    v16f& e1 = ga[1];
-    v16f& o0 = MX ? ga[0] : gb[0];
-    v16f& o1 = MX ? gc : gb[1];
-    iter(t, k1, k0, v2, v1, x0, x2, e0, e1, o0, o1, pa, pb, psa, psb);
-    if (t + 1 < n_steps) iter(t + 1, k2, k1, v0, v2, x1, x0, o0, o1, e0, e1, pb, pa, psb, psa);
-    if (t + 2 < n_steps) iter(t + 2, k0, k2, v1, v0, x2, x1, e0, e1, o0, o1, pa, pb, psa, psb);
-    if (t + 3 < n_steps) iter(t + 3, k1, k0, v2, v1, x0, x2, o0, o1, e0, e1, pb, pa, psb, psa);
-    if (t + 4 < n_steps) iter(t + 4, k2, k1, v0, v2, x1, x0, e0, e1, o0, o1, pa, pb, psa, psb);
-    if (t + 5 < n_steps) iter(t + 5, k0, k2, v1, v0, x2, x1, o0, o1, e0, e1, pb, pa, psb, psa);
-  }
-  // the last tile's product: V(n_steps - 1) sits in stage (n_steps - 1) % 3
-  {
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha_prev;
-    const int r = (n_steps - 1) % 3;
-    pv(r == 0 ? v0 : r == 1 ? v1 : v2, (n_steps & 1) ? pb : pa, (n_steps & 1) ? psb : psa);
-    // keep these MFMAs here, with every lane active: sunk into the store
-    // branch below they would run on a partial EXEC mask, which drops the
-    // operand rows of the inactive lanes
-#pragma unroll
-    for (int cb = 0; cb < DB; ++cb) asm volatile("" : "+v"(o[cb]));
-  }
-  wait_vm_le<0>();   // no copy may still target this workgroup's LDS when it ends
 
-  // ---- epilogue: O = acc / (448 l) / s_V (FP4 P.V: acc / l), stored through
-  // the output permutation
-  const float lt = swap_sum(l_run);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (myq < a.N) {
-    // row statistic for the backward pass: LSE = m + log2(sum_j 2^(S_j - m));
-    // l carries the factor 448 / 2^tau of the FP8 P (FP4 P.V: none)
-    if (a.lse && lg == 0)
-      a.lse[(int64_t)bh * a.N + myq] =
-          lt > 0.0f ? m_run + __log2f(lt) - (V4 ? 0.0f : kLog2_448 - a.tau) : kNegInf;
-    const int tok = a.out_perm ? a.out_perm[myq] : myq;
-    if (tok >= 0) {
-      const int b = bh / a.H, h = bh % a.H;
-      float* orow = a.out + b * a.osb + h * a.osh + (int64_t)tok * a.osn;
-      const float* vs = V4 ? nullptr : a.v_scale + (int64_t)bh * D;
-#pragma unroll
-      for (int cb = 0; cb < DB; ++cb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int c0 = 32 * cb + 8 * g4 + 4 * lg;
-          float4 r;
-          if (V4) {
-            r.x = o[cb][4 * g4 + 0] * inv;
-            r.y = o[cb][4 * g4 + 1] * inv;
-            r.z = o[cb][4 * g4 + 2] * inv;
-            r.w = o[cb][4 * g4 + 3] * inv;
+      // The previous tile's P.V and the next tile's S are independent MFMAs;
+      // they are dealt over 8 slots, one per group of 4 exponentials, and each
+      // slot's operands are read from LDS LA slots ahead (a slot is shorter
+      // than an LDS read's latency).  The order is pinned
+      // with empty volatile asm statements (kept in program order): a slot's
+      // MFMAs take their operands from one, and its exponentials end in one.
+      float gs[8];
+      float pq[4];   // exponentials of the previous group, packed one slot later
+      uint32_t pk4[4];   // FP4 P.V: E2M1 codes, 8 per dword, dwords 0-1 key group 0
+      // packs group g's four P values (E4M3, or E2M1 for FP4 P.V) and sums them;
+      // runs one slot after their exponentials so that the exp latency is hidden
+      // by other work
+      auto finish = [&](const int g) __attribute__((always_inline)) {
+        gs[g] = (pq[0] + pq[1]) + (pq[2] + pq[3]);
+        if (V4) {
+          uint32_t w;
+          if ((g & 1) == 0) {
+            asm volatile("" : "=v"(w));   // bytes 0-1 written here, 2-3 by group g + 1
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pq[0], pq[1], 1.0f, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pq[2], pq[3], 1.0f, 1);
           } else {
-            r.x = o[cb][4 * g4 + 0] * inv / vs[c0 + 0];
-            r.y = o[cb][4 * g4 + 1] * inv / vs[c0 + 1];
-            r.z = o[cb][4 * g4 + 2] * inv / vs[c0 + 2];
-            r.w = o[cb][4 * g4 + 3] * inv / vs[c0 + 3];
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk4[g / 2], pq[0], pq[1], 1.0f, 2);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pq[2], pq[3], 1.0f, 3);
           }
-          *reinterpret_cast<float4*>(orow + c0) = r;
+          asm volatile("" : "+v"(w), "+v"(gs[g]));
+          pk4[g / 2] = w;
+          return;
         }
+        int w;
+        asm volatile("" : "=v"(w));   // the two conversions below write all four bytes
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pq[0], pq[1], w, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pq[2], pq[3], w, true);
+        asm volatile("" : "+v"(w), "+v"(gs[g]));
+        pk[g] = w;
+      };
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        copy_item(g);
+#pragma unroll
+        for (int m = slot_lo(g); m < slot_lo(g + 1); ++m) {
+          if (MX && !V4 && m >= DB) {
+            // an E2M1 K operand lives in its lower four registers
+            v4i lo = {ops[m].a[0], ops[m].a[1], ops[m].a[2], ops[m].a[3]};
+            asm volatile("" : "+v"(lo));
+            ops[m].a[0] = lo[0]; ops[m].a[1] = lo[1]; ops[m].a[2] = lo[2]; ops[m].a[3] = lo[3];
+          } else {
+            asm volatile("" : "+v"(ops[m].a));
+          }
+          issue_op(m, ops[m], n0s, n1s, pk_in, vsc, ps_in);
+        }
+#pragma unroll
+        for (int m = slot_lo(g + LA); m < slot_lo(g + LA + 1); ++m) read_op(m, Vr, Kr, ops[m]);
+        const int kb = g / 4, g4 = g % 4;
+        const float cc = c[g];
+        const float sh = V4 ? mshg[kb] : msh;
+        float pn[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pn[j] = __builtin_amdgcn_exp2f(fmaf(s_cur(kb)[4 * g4 + j], cc, -sh));
+        if (g > 0) finish(g - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pq[j] = pn[j];
+      }
+      finish(7);
+      float sum;
+      if (V4) {
+        // B operand of the FP4 P.V product: lane half lg takes key group lg, its
+        // own 16 codes of that group and the other half's 16 (K slot order
+        // 8 b + r, then 8 b + 4 + r of the group, b, r < 4)
+        const auto t0 = __builtin_amdgcn_permlane32_swap(pk4[0], pk4[2], false, false);
+        const auto t1 = __builtin_amdgcn_permlane32_swap(pk4[1], pk4[3], false, false);
+        pk[0] = (int)t0[0]; pk[1] = (int)t1[0]; pk[2] = (int)t0[1]; pk[3] = (int)t1[1];
+        ps_out = 127 + (lg == 0 ? eg[0] : eg[1]);
+        sum = ldexpf((gs[0] + gs[1]) + (gs[2] + gs[3]), eg[0]) +
+              ldexpf((gs[4] + gs[5]) + (gs[6] + gs[7]), eg[1]);
+      } else {
+        sum = ((gs[0] + gs[1]) + (gs[2] + gs[3])) + ((gs[4] + gs[5]) + (gs[6] + gs[7]));
+      }
+      l_run = l_run * alpha + sum;
+      alpha_prev = alpha;
+      // K(t+2), V(t) and the side stage of t+1 must have landed; this
+      // iteration's copies may not have
+      wait_vm_le<NK + NV + NA>();
+      barrier_lds();
+    };
+    // unrolled by 6: the stage rings have period 3 and the two score buffers
+    // alternate, so no buffer is ever copied
+    for (int t = 0; t < n_steps; t += 6) {
+      // even t: S(t) in (ga0, ga1) -> S(t+1) in (MX ? ga0 : gb0, MX ? gc : gb1);
+      // odd t: S(t) in (MX ? ga0 : gb0, MX ? gc : gb1) -> S(t+1) in (ga0, ga1)
+      v16f& e0 = ga[0];
+      v16f& e1 = ga[1];
+      v16f& o0 = MX ? ga[0] : gb[0];
+      v16f& o1 = MX ? gc : gb[1];
+      iter(t, k1, k0, v2, v1, x0, x2, e0, e1, o0, o1, pa, pb, psa, psb);
+      if (t + 1 < n_steps) iter(t + 1, k2, k1, v0, v2, x1, x0, o0, o1, e0, e1, pb, pa, psb, psa);
+      if (t + 2 < n_steps) iter(t + 2, k0, k2, v1, v0, x2, x1, e0, e1, o0, o1, pa, pb, psa, psb);
+      if (t + 3 < n_steps) iter(t + 3, k1, k0, v2, v1, x0, x2, o0, o1, e0, e1, pb, pa, psb, psa);
+      if (t + 4 < n_steps) iter(t + 4, k2, k1, v0, v2, x1, x0, e0, e1, o0, o1, pa, pb, psa, psb);
+      if (t + 5 < n_steps) iter(t + 5, k0, k2, v1, v0, x2, x1, o0, o1, e0, e1, pb, pa, psb, psa);
     }
-  }
+    // the last tile's product: V(n_steps - 1) sits in stage (n_steps - 1) % 3
+    {
+#pragma unroll
+      for (int cb = 0; cb < DB; ++cb) o[cb] *= alpha_prev;
+      const int r = (n_steps - 1) % 3;
+      pv(r == 0 ? v0 : r == 1 ? v1 : v2, (n_steps & 1) ? pb : pa, (n_steps & 1) ? psb : psa);
+      // keep these MFMAs here, with every lane active: sunk into the store
+      // branch below they would run on a partial EXEC mask, which drops the
+      // operand rows of the inactive lanes
+#pragma unroll
+      for (int cb = 0; cb < DB; ++cb) asm volatile("" : "+v"(o[cb]));
+    }
+    wait_vm_le<0>();   // no copy may still target this workgroup's LDS when it ends
+
+    // ---- epilogue: O = acc / (448 l) / s_V (FP4 P.V: acc / l), stored through
+    // the output permutation
+    const float lt = swap_sum(l_run);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (myq < a.N) {
+      // row statistic for the backward pass: LSE = m + log2(sum_j 2^(S_j - m));
+      // l carries the factor 448 / 2^tau of the FP8 P (FP4 P.V: none)
+      if (a.lse && lg == 0)
+        a.lse[(int64_t)bh * a.N + myq] =
+            lt > 0.0f ? m_run + __log2f(lt) - (V4 ? 0.0f : kLog2_448 - a.tau) : kNegInf;
+      const int tok = a.out_perm ? a.out_perm[myq] : myq;
+      if (tok >= 0) {
+        const int b = bh / a.H, h = bh % a.H;
+        float* orow = a.out + b * a.osb + h * a.osh + (int64_t)tok * a.osn;
+        const float* vs = V4 ? nullptr : a.v_scale + (int64_t)bh * D;
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int c0 = 32 * cb + 8 * g4 + 4 * lg;
+            float4 r;
+            if (V4) {
+              r.x = o[cb][4 * g4 + 0] * inv;
+              r.y = o[cb][4 * g4 + 1] * inv;
+              r.z = o[cb][4 * g4 + 2] * inv;
+              r.w = o[cb][4 * g4 + 3] * inv;
+            } else {
+              r.x = o[cb][4 * g4 + 0] * inv / vs[c0 + 0];
+              r.y = o[cb][4 * g4 + 1] * inv / vs[c0 + 1];
+              r.z = o[cb][4 * g4 + 2] * inv / vs[c0 + 2];
+              r.w = o[cb][4 * g4 + 3] * inv / vs[c0 + 3];
+            }
+            *reinterpret_cast<float4*>(orow + c0) = r;
+          }
+      }
+    }
+    // every wave is done with this pass's stages before the next pass copies
+    // into them
+    if (pass + 1 < n_pass) barrier_lds();
+  }  // pass
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -1288,8 +1305,9 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 template <int D, bool MX, int MODE, bool V4>
 static hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const bool uk = MX || a.blk_k % kBN == 0;
-  const int64_t blocks = MODE == 2 ? (int64_t)a.B * a.H * a.n_tiles * (a.tile_tokens / kBM)
-                                   : (int64_t)a.B * a.H * a.n_qtiles;
+  const int64_t blocks = MODE == 2   ? (int64_t)a.B * a.H * a.n_tiles * (a.tile_tokens / kBM)
+                         : MODE == 1 ? (int64_t)a.B * a.H * ((a.n_qtiles + 1) / 2)
+                                     : (int64_t)a.B * a.H * a.n_qtiles;
   if (uk)
     hipLaunchKernelGGL((attn_fwd_kernel<D, MX, MODE, true, V4>), dim3((unsigned)blocks), dim3(256), 0, st,
                        a);
