@@ -670,8 +670,8 @@ __global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
           float cg = c[0] * gmax[kb];
           asm volatile("" : "+v"(cg));
           const float pmax = gmax[kb] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(cg - mnew);
-          const int eb = (int)(__float_as_uint(pmax) >> 23);
-          eg[kb] = eb == 0 ? -127 : max(eb - 129, -127);
+          const int eb = (int)(__float_as_uint(pmax) >> 23);   // 0 for 0 and subnormals
+          eg[kb] = max(eb - 129, -127);
           mshg[kb] = mnew == kNegInf ? 0.0f : mnew + (float)eg[kb];
         }
       }
