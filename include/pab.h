@@ -93,7 +93,8 @@ const char* pab_status_str(pab_status s);
 /* hipError_t of the last failing HIP call on this thread (0 if none). */
 int pab_last_hip_error(void);
 /* Token slots a quantised buffer for n tokens must hold (n rounded up to
- * PAB_TOKEN_ALIGN). */
+ * PAB_TOKEN_ALIGN; 0 for n <= 0, -1 when the rounded count is not
+ * representable). */
 int64_t pab_token_alloc(int64_t n);
 
 /* Tile sizes of the attention kernel for a recipe / head dim: BM queries per
@@ -311,7 +312,8 @@ pab_status pab_sta_steps(const int32_t* win_off, const int32_t* win_idx, int n_t
  * Strides must be multiples of 4 (float32) or 8 (bf16) elements and the
  * pointers 16-byte aligned.  PAB_UNSUPPORTED for d != 128, N > 2^20 or
  * B*H > 65536.
- * The workspace size is 0 for an empty input and -1 for a negative size.
+ * The workspace size is 0 for an empty input and -1 for a negative size or
+ * one beyond the backward's limits (B*H > 65536, N > 2^20, d > 128).
  */
 int64_t pab_attention_backward_workspace(int64_t B, int64_t H, int64_t N, int64_t d);
 pab_status pab_attention_backward(const pab_qview* q, const pab_qview* k, const pab_qview* v,

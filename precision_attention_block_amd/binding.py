@@ -211,7 +211,7 @@ def _lse_tensor(q, lse):
     import torch
     if lse is True:
         return torch.empty((q.B, q.H, q.N), dtype=torch.float32, device=q.codes.device)
-    return lse or None
+    return None if lse is None or lse is False else lse
 
 
 def key_tiles(kv_valid_host):

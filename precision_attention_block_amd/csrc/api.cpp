@@ -47,6 +47,7 @@ constexpr int64_t kMaxAttnTokens = (int64_t)1 << 22;   // N per head: bf16 K ope
 constexpr int64_t kMaxAttnRows = (int64_t)1 << 31;     // B*H*n_alloc (exclusive): 2 work-items per token slot
 constexpr int64_t kMaxGridY = 65536;                   // B*H of the quantiser and backward grids (y)
 constexpr int64_t kMaxQuantTokens = (int64_t)1 << 27;  // n_out: up to 16 work-items per token slot
+constexpr int64_t kMaxBwdTokens = (int64_t)1 << 20;    // N of the backward
 
 // Validates a quantised operand view; `role` 0 = Q/K, 1 = V.  An FP8 Q/K
 // view must carry its bf16 operand copy when `need_operand` is set (the
@@ -55,7 +56,9 @@ constexpr int64_t kMaxQuantTokens = (int64_t)1 << 27;  // n_out: up to 16 work-i
 pab_status check_view(const pab_qview* v, int role, bool need_operand = true) {
   if (!v || !v->codes || !v->scales) return PAB_INVALID_ARG;
   if (v->B < 1 || v->H < 1 || v->N < 1 || v->d < 1) return PAB_INVALID_ARG;
-  if (v->B * v->H > (int64_t)1 << 24 || v->N > kMaxAttnTokens) return PAB_UNSUPPORTED;
+  if (v->B > (int64_t)1 << 24 || v->H > (int64_t)1 << 24 || v->B * v->H > (int64_t)1 << 24 ||
+      v->N > kMaxAttnTokens)
+    return PAB_UNSUPPORTED;
   if (v->B * v->H * round_up(v->N, PAB_TOKEN_ALIGN) >= kMaxAttnRows) return PAB_UNSUPPORTED;
   if (!aligned(v->codes, 16)) return PAB_INVALID_ARG;
   if (role == 1) {
@@ -169,7 +172,11 @@ const char* pab_status_str(pab_status s) {
 
 int pab_last_hip_error(void) { return g_last_hip_error; }
 
-int64_t pab_token_alloc(int64_t n) { return n <= 0 ? 0 : round_up(n, PAB_TOKEN_ALIGN); }
+int64_t pab_token_alloc(int64_t n) {
+  if (n <= 0) return 0;
+  if (n > INT64_MAX - (PAB_TOKEN_ALIGN - 1)) return -1;   // not representable
+  return round_up(n, PAB_TOKEN_ALIGN);
+}
 
 pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, int* BN) {
   if (!BM || !BN) return PAB_INVALID_ARG;
@@ -397,6 +404,8 @@ pab_status pab_sta_steps(const int32_t* win_off, const int32_t* win_idx, int n_t
 int64_t pab_attention_backward_workspace(int64_t B, int64_t H, int64_t N, int64_t d) {
   if (B < 0 || H < 0 || N < 0 || d < 1) return -1;
   if (B == 0 || H == 0 || N == 0) return 0;
+  if (B > kMaxGridY || H > kMaxGridY || B * H > kMaxGridY || N > kMaxBwdTokens || d > 128)
+    return -1;
   int64_t off[13];
   return pab::bwd_workspace_layout(B * H, round_up(N, PAB_TOKEN_ALIGN), d, off);
 }
@@ -421,7 +430,7 @@ static pab_status backward_impl(const pab_qview* q, const pab_qview* k, const pa
   if (q->B != k->B || q->B != v->B || q->H != k->H || q->H != v->H || q->N != k->N ||
       q->N != v->N || q->d != k->d || q->d != v->d)
     return PAB_INVALID_ARG;
-  if (q->d != 128 || q->N > ((int64_t)1 << 20) || q->B * q->H > kMaxGridY) return PAB_UNSUPPORTED;
+  if (q->d != 128 || q->N > kMaxBwdTokens || q->B * q->H > kMaxGridY) return PAB_UNSUPPORTED;
   if (dout_dtype != PAB_F32 && dout_dtype != PAB_BF16) return PAB_INVALID_ARG;
   if (!out || !out_strides || !dout || !dout_strides || !lse || !dq || !dk || !dv ||
       !grad_strides || !workspace)
@@ -630,8 +639,8 @@ pab_status pab_sta_plan(const int grid[3], const int real_grid[3], const int til
     tokens *= grid[i];
     tiles *= nt[i];
     real *= real_grid[i];
+    if (tokens > (int64_t)1 << 30) return PAB_UNSUPPORTED;   // checked per axis: no overflow
   }
-  if (tokens > (int64_t)1 << 30) return PAB_UNSUPPORTED;
   // window size per tile: product over axes of the clipped interval length
   auto axis_count = [&](int a, int c) {
     return std::min(c + rad[a], nt[a] - 1) - std::max(c - rad[a], 0) + 1;
