@@ -872,16 +872,18 @@ struct PP {
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
-template <bool MX, typename KPlan>
+// koff: the lane offset of this wave's K copy instructions (wave + 8 j has
+// the swizzle phase of the wave for every j).
+template <bool MX>
 __device__ inline void pp_issue_k(uint8_t* kbuf, const HeadBuffers& hb, int ks, int wave, int lane,
-                                  const KPlan& kp) {
+                                  uint32_t koff) {
   using TL = typename PP<MX>::TL;
-  constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI, KPER = DmaPlan<TL::K_CPR>::PER;
+  constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI;
   if (MX) {
     if (wave < 4) {
       const int inst = wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16,
-                                               kp.off[inst % KPER], (ks + inst * KRPI) * TL::KROW, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16, koff,
+                                               (ks + inst * KRPI) * TL::KROW, 0, 0);
     } else {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(kbuf + TL::K_BYTES), 4, 4 * lane,
                                                ks * (PP<MX>::D / 32), 0, 0);
@@ -890,8 +892,8 @@ __device__ inline void pp_issue_k(uint8_t* kbuf, const HeadBuffers& hb, int ks, 
 #pragma unroll
     for (int j = 0; j < PP<MX>::KI8; ++j) {
       const int inst = wave + 8 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16,
-                                               kp.off[inst % KPER], (ks + inst * KRPI) * TL::KROW, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16, koff,
+                                               (ks + inst * KRPI) * TL::KROW, 0, 0);
     }
   }
 }
@@ -987,6 +989,14 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   DmaPlan<4> vp;
   kp.init(lane, TL::KROW);
   vp.init(lane, a.n_alloc);
+  // every K copy instruction of this wave (wave + 8 j) has the swizzle phase
+  // wave % PER: its lane offset is chosen once, with uniform selects (an
+  // index into kp.off would be a dynamic one, and the array would be placed in
+  // LDS and read back on every copy)
+  constexpr int KPER = DmaPlan<TL::K_CPR>::PER;
+  uint32_t koff = kp.off[0];
+#pragma unroll
+  for (int p = 1; p < KPER; ++p) koff = wave % KPER == p ? kp.off[p] : koff;
   HeadBuffers hb;
   hb.k = __builtin_amdgcn_make_buffer_rsrc((void*)kbh, 0, a.n_alloc * TL::KROW, kRsrcWord3);
   hb.v = __builtin_amdgcn_make_buffer_rsrc((void*)vbh, 0, a.n_alloc * D, kRsrcWord3);
@@ -1017,21 +1027,21 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   // issued back to back by every wave they would queue up at the texture
   // unit and stall the issuing waves.
   auto copy_item = [&](const int j, const int t, const int r) __attribute__((always_inline)) {
-    constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI, KPER = DmaPlan<TL::K_CPR>::PER;
+    constexpr int KRPI = DmaPlan<TL::K_CPR>::RPI;
     uint8_t* kbuf = KS[(r + 3) & 3];
     const int ks_k = key_at(t + 3), ks_a = key_at(t + 2);
     if (j < P::KI8) {
       if (MX) {
         if (wave < 4)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + wave * 1024), 16,
-                                                   kp.off[wave % KPER], (ks_k + wave * KRPI) * TL::KROW, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + wave * 1024), 16, koff,
+                                                   (ks_k + wave * KRPI) * TL::KROW, 0, 0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.s, (lds_void_t*)(kbuf + TL::K_BYTES), 4, 4 * lane,
                                                    ks_k * (D / 32), 0, 0);
       } else {
         const int inst = wave + 8 * j;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16,
-                                                 kp.off[inst % KPER], (ks_k + inst * KRPI) * TL::KROW, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hb.k, (lds_void_t*)(kbuf + inst * 1024), 16, koff,
+                                                 (ks_k + inst * KRPI) * TL::KROW, 0, 0);
       }
     } else if (j == P::KI8) {
       pp_issue_v<MX>(VS[(r + 2) & 3], hb, a.n_alloc, key_at(t + 2), wave, vp);
@@ -1237,7 +1247,7 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 
   // ---- prologue: K(0..2), V(0..1), side data of tiles 0 and 1; S(0)
 #pragma unroll
-  for (int t = 0; t < 3; ++t) pp_issue_k<MX>(KS[t], hb, key_at(t), wave, lane, kp);
+  for (int t = 0; t < 3; ++t) pp_issue_k<MX>(KS[t], hb, key_at(t), wave, lane, koff);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     pp_issue_v<MX>(VS[t], hb, a.n_alloc, key_at(t), wave, vp);
