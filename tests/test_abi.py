@@ -46,6 +46,10 @@ def test_probe_library_exports_its_header():
 
 def test_token_alloc_and_info(B):
     assert B.token_alloc(1) == 128 and B.token_alloc(128) == 128 and B.token_alloc(129) == 256
+    assert B.token_alloc(0) == 0 and B.token_alloc(-7) == 0
+    assert B.token_alloc(2 ** 63 - 1) == -1                 # rounding up would overflow
+    assert B.backward_workspace_bytes(1, 1, 2 ** 62, 128) == -1
+    assert B.backward_workspace_bytes(2 ** 40, 2 ** 40, 128, 128) == -1
     assert B.attention_info("fp8_block", 128, 0) == (256, 64)
     assert B.attention_info("fp8_block", 128, 1) == (128, 64)
     assert B.attention_info("fp8_block", 128, 2) == (128, 64)
