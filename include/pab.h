@@ -383,8 +383,10 @@ pab_status pab_attention_sta_backward(const pab_qview* q, const pab_qview* k, co
  * in raster order, tile = (t, h, w) tokens per tile, window = (w_t, w_h, w_w)
  * in tiles: key tile v is in the window of query tile u iff
  * |u_a - v_a| <= floor(w_a / 2) on every axis, clipped at the grid border.
- * Kernel token order: tiles in raster order over the tile grid, tokens in
- * raster order inside a tile.
+ * Kernel token order: tiles in raster order over the tile grid; inside a
+ * tile its real tokens in raster order, then its padding slots (so padding
+ * fills whole key steps and query tiles where it can, which the step lists
+ * and the query-tile skip then leave out).
  * Outputs (host memory; pass NULL to skip an array; call once with all NULL
  * to get the sizes):
  *   perm       int32 [n_tokens]: raster index in real_grid of kernel token p,

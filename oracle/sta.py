@@ -11,8 +11,10 @@ Readings (the printed window formula is garbled):
   * window sizes are given in tiles per axis, w = (w_t, w_h, w_w); v is in W(u)
     iff |u_a - v_a| <= floor(w_a / 2) on every axis; windows are clipped at the
     grid border (not shifted);
-  * kernel token order: tiles in raster order over (tile_t, tile_h, tile_w),
-    tokens inside a tile in raster order over (dt, dh, dw);
+  * kernel token order: tiles in raster order over (tile_t, tile_h, tile_w);
+    inside a tile its real tokens in raster order over (dt, dh, dw), then its
+    padding slots (the pages make each tile contiguous and leave the order
+    inside it open; padding last fills whole key steps and query tiles);
   * a grid that is not a multiple of the tile is zero-padded at the high end;
     padded tokens are not keys (masked) and their outputs are not stored.
 """
@@ -45,12 +47,12 @@ def plan(grid, real_grid, tile, window):
     tiles = list(itertools.product(range(nt), range(nh), range(nw)))
     perm = []
     for (ut, uh, uw) in tiles:
+        real = []
         for (dt, dh, dw) in itertools.product(range(tt), range(th), range(tw)):
             t, h, w = ut * tt + dt, uh * th + dh, uw * tw + dw
             if t < Tr and h < Hr and w < Wr:
-                perm.append((t * Hr + h) * Wr + w)
-            else:
-                perm.append(-1)
+                real.append((t * Hr + h) * Wr + w)
+        perm += real + [-1] * (tt * th * tw - len(real))
     perm = np.array(perm, dtype=np.int32)
     rad = [wa // 2 for wa in window]
     off, idx = [0], []

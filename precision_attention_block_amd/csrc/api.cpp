@@ -655,20 +655,31 @@ pab_status pab_sta_plan(const int grid[3], const int real_grid[3], const int til
   if (n_pairs) *n_pairs = pairs;
 
   if (perm || inv_perm || kv_valid) {
-    int64_t p = 0;
+    // inside a tile its real tokens come first, in raster order, and its
+    // padding slots last, so that padding fills whole key steps and query
+    // tiles wherever it can
+    const int64_t tile_tokens = (int64_t)tile[0] * tile[1] * tile[2];
+    int64_t base = 0;
     for (int ut = 0; ut < nt[0]; ++ut)
       for (int uh = 0; uh < nt[1]; ++uh)
-        for (int uw = 0; uw < nt[2]; ++uw)
+        for (int uw = 0; uw < nt[2]; ++uw, base += tile_tokens) {
+          int64_t p = base;
           for (int dt = 0; dt < tile[0]; ++dt)
             for (int dh = 0; dh < tile[1]; ++dh)
-              for (int dw = 0; dw < tile[2]; ++dw, ++p) {
+              for (int dw = 0; dw < tile[2]; ++dw) {
                 const int t = ut * tile[0] + dt, h = uh * tile[1] + dh, w = uw * tile[2] + dw;
-                const bool ok = t < real_grid[0] && h < real_grid[1] && w < real_grid[2];
-                const int64_t r = ok ? ((int64_t)t * real_grid[1] + h) * real_grid[2] + w : -1;
+                if (t >= real_grid[0] || h >= real_grid[1] || w >= real_grid[2]) continue;
+                const int64_t r = ((int64_t)t * real_grid[1] + h) * real_grid[2] + w;
                 if (perm) perm[p] = (int32_t)r;
-                if (kv_valid) kv_valid[p] = ok ? 1 : 0;
-                if (inv_perm && ok) inv_perm[r] = (int32_t)p;
+                if (kv_valid) kv_valid[p] = 1;
+                if (inv_perm) inv_perm[r] = (int32_t)p;
+                ++p;
               }
+          for (; p < base + tile_tokens; ++p) {
+            if (perm) perm[p] = -1;
+            if (kv_valid) kv_valid[p] = 0;
+          }
+        }
   }
   if (win_off || win_idx || lpt_order) {
     std::vector<int32_t> sizes(tiles);
