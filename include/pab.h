@@ -98,11 +98,11 @@ int pab_last_hip_error(void);
 int64_t pab_token_alloc(int64_t n);
 
 /* Tile sizes of the attention kernel for a recipe / head dim: BM queries per
- * workgroup (256 for dense FP8 attention with d = 128, else 128), BN keys per
- * online-softmax step (64).  The online softmax visits key
- * tiles of BN keys in ascending order and requantises P against the running
- * maximum including the current tile, so BN is part of the result's
- * definition (the reference oracle takes it as a parameter).
+ * workgroup (256 for dense FP8 attention with d = 128 over all key tiles,
+ * mode 0; else 128), BN keys per online-softmax step (64).  The online
+ * softmax visits key tiles of BN keys in ascending order and requantises P
+ * against the running maximum including the current tile, so BN is part of
+ * the result's definition (the reference oracle takes it as a parameter).
  * mode: 0 dense, 1 causal, 2 sliding-tile, 3 dense over listed key tiles. */
 pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, int* BN);
 

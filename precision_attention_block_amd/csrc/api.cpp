@@ -188,9 +188,9 @@ pab_status pab_attention_info(pab_recipe qk_recipe, int d, int mode, int* BM, in
   } else {
     return PAB_INVALID_ARG;
   }
-  // dense FP8 attention with d = 128 runs the 8-wave kernel (256 queries)
-  *BM = (qk_recipe == PAB_FP8_TOKEN_BLOCK && d == 128 && (mode == 0 || mode == 3)) ? 2 * pab::kBM
-                                                                                 : pab::kBM;
+  // dense FP8 attention with d = 128 over all key tiles runs the 8-wave
+  // kernel (256 queries)
+  *BM = (qk_recipe == PAB_FP8_TOKEN_BLOCK && d == 128 && mode == 0) ? 2 * pab::kBM : pab::kBM;
   *BN = pab::kBN;
   return PAB_OK;
 }

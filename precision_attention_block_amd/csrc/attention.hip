@@ -843,9 +843,10 @@ __global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong variant for dense attention with d = 128, over all key tiles or
-// the listed ones (mode 3).  It also handles the causal mask, which the
-// dispatch gives to the 4-wave kernel (faster there).
+// Ping-pong variant for dense attention with d = 128 over all key tiles
+// (optionally with a key padding mask).  Causal attention and the listed key
+// tiles of padded grids go to the 4-wave kernel, which measures faster there
+// (it pairs causal tiles and skips query tiles that hold only padding).
 //
 // A workgroup of 8 waves owns 256 queries of one head (32 per wave).  Waves w
 // and w + 4 share a SIMD; they form two groups that alternate between a
@@ -915,7 +916,7 @@ __device__ inline void pp_issue_v(uint8_t* vbuf, const HeadBuffers& hb, int n_al
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <bool MX, int MODE, bool UK>
+template <bool MX, bool UK>
 __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using P = PP<MX>;
@@ -937,19 +938,11 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
   const int work = xcd_work_index(blockIdx.x, gridDim.x);
   const int n_qt = (a.n_alloc + P::BMW - 1) / P::BMW;
   const int bh = work / n_qt;
-  int qt = work % n_qt;
-  if (MODE == 1) qt = n_qt - 1 - qt;   // longest query tiles first
-  const int q0 = qt * P::BMW;
-  const int all = (a.N + kBN - 1) / kBN;
-  const int n_steps = MODE == 1 ? min((q0 + P::BMW) / kBN, all) : MODE == 3 ? a.n_key_tiles : all;
-  // first key of step t: MODE 3 visits the listed key tiles only (past the
-  // last step, the last listed tile again: those copies land in stages that
-  // are never read)
-  typedef const __attribute__((address_space(4))) int32_t const_i32;
-  const_i32* klist = MODE == 3 ? (const_i32*)a.key_tiles : nullptr;
-  auto key_at = [&](int t) __attribute__((always_inline)) -> int {
-    return MODE == 3 ? klist[min(t, n_steps - 1)] * kBN : t * kBN;
-  };
+  const int q0 = (work % n_qt) * P::BMW;
+  const int n_steps = (a.N + kBN - 1) / kBN;
+  // first key of step t (past the last step: copies of keys past N, which
+  // read zeros into stages that are never read)
+  auto key_at = [&](int t) __attribute__((always_inline)) -> int { return t * kBN; };
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + lr;
   const bool q_live = wq0 < a.n_alloc;      // the wave's 32 queries have token slots
@@ -1176,11 +1169,11 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
         c[g] = cq * __builtin_amdgcn_rcpf(Cs[key / a.blk_k - ks / a.blk_k]);
       }
     }
-    const bool edge = (ks + kBN > a.N) || (MODE == 1 && ks + kBN - 1 > wq0);
+    const bool edge = ks + kBN > a.N;
     if (edge || hb.has_mask) {
       const bool partial = hb.has_mask && Ar[lane] == 0;
       if (edge || __builtin_amdgcn_ballot_w64(partial) != 0) {
-        const int lim = MODE == 1 ? min(a.N - 1, myq) : a.N - 1;
+        const int lim = a.N - 1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1343,25 +1336,23 @@ static hipError_t launch_mode(const AttnArgs& a, int mode, hipStream_t st) {
   return launch_t<D, MX, 0, V4>(a, st);
 }
 
-template <bool MX, int MODE>
+template <bool MX>
 static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
   const bool uk = MX || a.blk_k % kBN == 0;
   const int64_t blocks = (int64_t)a.B * a.H * ((a.n_alloc + PP<MX>::BMW - 1) / PP<MX>::BMW);
   if (uk)
-    hipLaunchKernelGGL((attn_pp_kernel<MX, MODE, true>), dim3((unsigned)blocks), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((attn_pp_kernel<MX, true>), dim3((unsigned)blocks), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_pp_kernel<MX, MODE, false>), dim3((unsigned)blocks), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((attn_pp_kernel<MX, false>), dim3((unsigned)blocks), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs& a, int d, bool mx, bool v4, int mode, hipStream_t st) {
-  // mode 3 (dense over listed key tiles) takes the same kernel as dense
   // dense FP8 with d = 128: the ping-pong kernel (its matrix phase, with QK^T
-  // on the bf16 MFMA, is long enough to balance the vector phase; for MXFP4
-  // and for causal masks the 4-wave kernel measures faster)
+  // on the bf16 MFMA, is long enough to balance the vector phase; for MXFP4,
+  // causal masks and listed key tiles the 4-wave kernel measures faster)
   if (v4) return mx && d == 128 ? launch_mode<128, true, true>(a, mode, st) : hipErrorInvalidValue;
-  if (!mx && d == 128 && mode == 0) return launch_pp<false, 0>(a, st);
-  if (!mx && d == 128 && mode == 3) return launch_pp<false, 3>(a, st);
+  if (!mx && d == 128 && mode == 0) return launch_pp<false>(a, st);
   if (mx) return launch_mode<128, true>(a, mode, st);
   if (d == 64) return launch_mode<64, false>(a, mode, st);
   return launch_mode<128, false>(a, mode, st);
