@@ -169,6 +169,49 @@ def test_sta_parity_with_padding(gpu_lib, window, tau):
     assert np.array_equal(_run_sta(gpu_lib, hp, ts, tau=tau, steps=True), got)
 
 
+@pytest.mark.parametrize("recipe", ["fp8", "mxfp4"])
+def test_sta_batch_of_two(gpu_lib, recipe):
+    """Sliding-tile attention with B = 2 on a padded grid: every (b, h) slice
+    matches the oracle, in the caller's token order and through strided output
+    (the kernel's batch and head offsets of inputs, outputs and the row
+    statistic)."""
+    grid, real, tile, window = (4, 16, 16), (3, 15, 13), (2, 8, 8), (1, 3, 3)
+    hp = gpu_lib.sta_plan(grid, real, tile, window)
+    op = OS.plan(grid, real, tile, window)
+    dp = gpu_lib.DevicePlan(hp)
+    n_real = int(np.prod(real))
+    B, H = 2, 2
+    x, ts = _inputs(B, H, n_real, 128, 44, torch.bfloat16, True)
+    dev = [t.cuda() for t in ts]
+    blk = hp.tile_tokens if recipe == "fp8" else None
+    qr = "fp8_block" if recipe == "fp8" else "mxfp4"
+    q = gpu_lib.quantize(dev[0], qr, blk, perm=dp.perm, n_out=dp.n_tokens, operand=False)
+    k = gpu_lib.quantize(dev[1], qr, blk, perm=dp.perm, n_out=dp.n_tokens)
+    v = gpu_lib.quantize(dev[2], "fp8_channel", perm=dp.perm, n_out=dp.n_tokens)
+    buf = torch.full((B, n_real, H, 128), float("nan"), device="cuda")
+    got = gpu_lib.attention_sta(q, k, v, dp, out=buf.permute(0, 2, 1, 3), steps=True)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    _, bn = gpu_lib.attention_info(qr, 128, 2)
+    xk = [OS.gather_tokens(a, op.perm) for a in x]
+    ops = oracle_operands(*xk, recipe, op.tile_tokens)
+    ref = np.full_like(got, np.nan)
+    tt = op.tile_tokens
+    for b in range(B):
+        for h in range(H):
+            qo, ko, vo = ops[b][h]
+            for u in range(op.n_tiles):
+                rows = np.arange(u * tt, (u + 1) * tt)
+                keep = op.perm[rows] >= 0
+                if not keep.any():
+                    continue
+                o = OA.recipe_attention(qo, ko, vo, rows[keep], sm_scale=1 / np.sqrt(128), bn=bn,
+                                        kv_valid=op.kv_valid, key_blocks=OS.key_blocks_for_tile(op, u, bn))
+                ref[b, h, op.perm[rows][keep]] = o
+    assert not np.isnan(got).any()
+    assert_close(got, ref, "sta B=2 %s" % recipe)
+
+
 @pytest.mark.parametrize("grid,real,tile,window", [
     ((8, 16, 24), (7, 15, 22), (4, 8, 8), (3, 3, 3)),          # 256-token tiles
     ((6, 32, 32), (5, 30, 31), (6, 16, 16), (1, 3, 3)),        # 1536-token tiles
