@@ -831,7 +831,7 @@ __global__ __launch_bounds__(256, MX ? 3 : 2) void attn_fwd_kernel(AttnArgs a) {
               r.z = o[cb][4 * g4 + 2] * inv / vs[c0 + 2];
               r.w = o[cb][4 * g4 + 3] * inv / vs[c0 + 3];
             }
-            *reinterpret_cast<float4*>(orow + c0) = r;
+            store4_stream(orow + c0, r.x, r.y, r.z, r.w);
           }
       }
     }
@@ -1301,12 +1301,8 @@ __global__ __launch_bounds__(512, 1) void attn_pp_kernel(AttnArgs a) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int c0 = 32 * cb + 8 * g4 + 4 * lg;
-          float4 r;
-          r.x = o[cb][4 * g4 + 0] * inv / vs[c0 + 0];
-          r.y = o[cb][4 * g4 + 1] * inv / vs[c0 + 1];
-          r.z = o[cb][4 * g4 + 2] * inv / vs[c0 + 2];
-          r.w = o[cb][4 * g4 + 3] * inv / vs[c0 + 3];
-          *reinterpret_cast<float4*>(orow + c0) = r;
+          store4_stream(orow + c0, o[cb][4 * g4 + 0] * inv / vs[c0 + 0], o[cb][4 * g4 + 1] * inv / vs[c0 + 1],
+                        o[cb][4 * g4 + 2] * inv / vs[c0 + 2], o[cb][4 * g4 + 3] * inv / vs[c0 + 3]);
         }
     }
   }
