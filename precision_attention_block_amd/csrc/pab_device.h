@@ -14,13 +14,8 @@ constexpr float kE4M3Max = 448.0f;
 constexpr float kLog2_448 = 8.807354922057604f;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Stores four floats with the non-temporal hint: the attention output is
-// written once and not read back by the kernel, and a plain store would keep
-// its lines in the L2 at the expense of the K and V tiles every workgroup of
-// the head still reads (measured: the dense MXFP4 16K launch fetched half the
-// bytes from memory with it, 0.26 instead of 0.53 GB).
-__device__ inline void store4_stream(float* p, float x, float y, float z, float w) {
-  const v4f v = {x, y, z, w};
+// Stores four floats with the non-temporal hint (see store_o_rows).
+__device__ inline void store4_stream(float* p, v4f v) {
   __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
 }
 
