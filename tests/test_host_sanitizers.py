@@ -7,11 +7,10 @@ linked into tests/host_sanitize_driver.cpp, which runs the sliding-tile
 planner, the step and key-tile helpers and the size helpers on valid and
 hostile sizes with exact-size output arrays, and every validation path of the
 device entry points with arguments that must be rejected before the first HIP
-call.  Any sanitizer report aborts the driver; the test also requires the
-driver's own checks to pass.
+call.  Any sanitizer report aborts that program; the test also requires its
+own checks to pass.
 """
 import os
-import shutil
 import subprocess
 
 import pytest
