@@ -75,6 +75,30 @@ def test_dense_parity(gpu_lib, case):
     print("  max-abs %.3g mean-abs %.3g" % (mx, mean))
 
 
+@pytest.mark.parametrize("N", [1, 33, 65, 129, 257])
+@pytest.mark.parametrize("recipe,d,causal", [("fp8", 128, False), ("fp8", 128, True), ("fp8", 64, False),
+                                             ("mxfp4", 128, False), ("mxfp4", 128, True)])
+def test_short_sequences(gpu_lib, N, recipe, d, causal):
+    """Token counts of one, and just past a key step or a query tile: the
+    last tile's rows past N are neither computed into nor stored (every
+    output element is written, none past the tensor)."""
+    print("short", N, recipe, d, causal, flush=True)
+    x, ts = _inputs(1, 2, N, d, 700 + N, torch.bfloat16, True)
+    _, bn = gpu_lib.attention_info("mxfp4" if recipe == "mxfp4" else "fp8_block", d, 1 if causal else 0)
+    blk = 64 if recipe == "fp8" else None
+    dev = [t.cuda() for t in ts]
+    qr = "fp8_block" if recipe == "fp8" else "mxfp4"
+    q, k = (gpu_lib.quantize(t, qr, blk) for t in dev[:2])
+    v = gpu_lib.quantize(dev[2], "fp8_channel")
+    out = torch.full((1, 2, N, d), float("nan"), device="cuda")
+    gpu_lib.attention_dense(q, k, v, causal=causal, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert not np.isnan(got).any()
+    ref = _oracle_dense(x, recipe, blk, causal, 1 / np.sqrt(d), bn)
+    assert_close(got, ref, "short N=%d %s d=%d causal=%s" % (N, recipe, d, causal))
+
+
 @pytest.mark.parametrize("tau", [2, 8])
 @pytest.mark.parametrize("case", [
     dict(recipe="fp8", d=128, N=1000, causal=False, blk=128),
