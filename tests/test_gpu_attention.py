@@ -193,6 +193,41 @@ def test_sta_parity_with_padding(gpu_lib, window, tau):
     assert np.array_equal(_run_sta(gpu_lib, hp, ts, tau=tau, steps=True), got)
 
 
+@pytest.mark.parametrize("steps", [False, True])
+def test_sta_head_dim_64(gpu_lib, steps):
+    """Sliding-tile FP8 attention with d = 64 on a padded grid (the 4-wave
+    kernel's d = 64 instance), window lists in tiles and in key steps."""
+    grid, real, tile, window = (4, 16, 16), (3, 14, 16), (2, 8, 8), (1, 3, 3)
+    hp = gpu_lib.sta_plan(grid, real, tile, window)
+    op = OS.plan(grid, real, tile, window)
+    dp = gpu_lib.DevicePlan(hp)
+    n_real = int(np.prod(real))
+    x, ts = _inputs(1, 2, n_real, 64, 45, torch.bfloat16, True)
+    dev = [t.cuda() for t in ts]
+    q = gpu_lib.quantize(dev[0], "fp8_block", hp.tile_tokens, perm=dp.perm, n_out=dp.n_tokens)
+    k = gpu_lib.quantize(dev[1], "fp8_block", hp.tile_tokens, perm=dp.perm, n_out=dp.n_tokens)
+    v = gpu_lib.quantize(dev[2], "fp8_channel", perm=dp.perm, n_out=dp.n_tokens)
+    got = gpu_lib.attention_sta(q, k, v, dp, steps=steps)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    _, bn = gpu_lib.attention_info("fp8_block", 64, 2)
+    xk = [OS.gather_tokens(a, op.perm) for a in x]
+    ops = oracle_operands(*xk, "fp8", op.tile_tokens)
+    ref = np.full_like(got, np.nan)
+    tt = op.tile_tokens
+    for h in range(2):
+        qo, ko, vo = ops[0][h]
+        for u in range(op.n_tiles):
+            rows = np.arange(u * tt, (u + 1) * tt)
+            keep = op.perm[rows] >= 0
+            if not keep.any():
+                continue
+            o = OA.recipe_attention(qo, ko, vo, rows[keep], sm_scale=1 / np.sqrt(64), bn=bn,
+                                    kv_valid=op.kv_valid, key_blocks=OS.key_blocks_for_tile(op, u, bn))
+            ref[0, h, op.perm[rows][keep]] = o
+    assert_close(got, ref, "sta d=64 steps=%s" % steps)
+
+
 @pytest.mark.parametrize("recipe", ["fp8", "mxfp4"])
 def test_sta_batch_of_two(gpu_lib, recipe):
     """Sliding-tile attention with B = 2 on a padded grid: every (b, h) slice
