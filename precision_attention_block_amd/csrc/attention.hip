@@ -42,7 +42,13 @@
 //  * workgroups are dealt to XCDs so that all query tiles of a head share an
 //    L2; a causal workgroup computes a long and a short query tile of its
 //    head in turn (tiles n - 1 - p and p), so all causal workgroups carry the
-//    same work and the launch has no tail of short tiles.
+//    same work and the launch has no tail of short tiles (FP8 and FP4 P.V;
+//    see the pairing note in the kernel).
+//  * a workgroup whose queries are all padding ends at once; the output is
+//    staged through LDS and written with streaming stores of whole 128-byte
+//    row segments (store_o_rows).
+// Dense FP8 attention with d = 128 over all key tiles runs on the ping-pong
+// kernel further below instead.
 #include "pab_device.h"
 #include "pab_internal.h"
 #include "pab_lds.h"
