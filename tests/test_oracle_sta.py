@@ -49,6 +49,24 @@ def test_permutation_and_padding():
     assert np.array_equal(t, np.repeat(np.arange(6), 64))
     assert np.array_equal(h, np.tile(np.repeat(np.arange(8), 8), 6))
     assert np.array_equal(w, np.tile(np.arange(8), 48))
+    # a tile cut by the grid's end along h (tile rows 40..47, real rows 0..44):
+    # its 5 x 8 real positions of each of its 6 frames first, in raster order,
+    # then its 144 padding slots
+    u = 5 * 10 + 3                      # tile (0, 5, 3)
+    blk = p.perm[u * 384:(u + 1) * 384]
+    t, rem = np.divmod(blk[:240], 45 * 80)
+    h, w = np.divmod(rem, 80)
+    assert np.array_equal(t, np.repeat(np.arange(6), 40))
+    assert np.array_equal(h, np.tile(np.repeat(np.arange(40, 45), 8), 6))
+    assert np.array_equal(w, np.tile(np.arange(24, 32), 30))
+    assert np.all(blk[240:] == -1)
+    # every tile: its real tokens are exactly the real points of its 3D box
+    for u in range(p.n_tiles):
+        ut, uh, uw = u // 60, (u // 10) % 6, u % 10
+        box = [(tt * 45 + hh) * 80 + ww for tt in range(6 * ut, min(6 * ut + 6, 21))
+               for hh in range(8 * uh, min(8 * uh + 8, 45)) for ww in range(8 * uw, 8 * uw + 8)]
+        blk = p.perm[u * 384:(u + 1) * 384]
+        assert np.array_equal(blk[:len(box)], np.array(box)) and np.all(blk[len(box):] == -1)
     # gather puts zeros at padding positions
     x = np.arange(21 * 45 * 80, dtype=np.float32)[None, :, None]
     g = S.gather_tokens(x, p.perm)
