@@ -53,6 +53,7 @@ def test_token_alloc_and_info(B):
     assert B.attention_info("fp8_block", 128, 0) == (256, 64)
     assert B.attention_info("fp8_block", 128, 1) == (128, 64)
     assert B.attention_info("fp8_block", 128, 2) == (128, 64)
+    assert B.attention_info("fp8_block", 128, 3) == (128, 64)   # listed key steps: 4-wave kernel
     assert B.attention_info("fp8_block", 64, 0) == (128, 64)
     assert B.attention_info("mxfp4", 128, 0) == (128, 64)
     assert B.attention_info("mxfp4", 128, 1)[1] == 64
